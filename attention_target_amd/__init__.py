@@ -1,0 +1,248 @@
+"""Python binding of libkvpop.so, the MI355X (gfx950) library for the KVpop
+future-attention target and fixed-budget sparse attention.
+
+The binding only marshals arguments: every step of the computation runs in
+the HIP kernels behind the C ABI declared in include/kvpop.h.  PyTorch is used
+for device memory and streams.  There is no fallback: if the library is not
+built, or no GPU is present, the calls raise.
+
+Entry points (same names as the C ABI, without the ``kvpop_`` prefix):
+    attn_fwd_lse(q, k, v, ...)            -> (o, lse)
+    future_target(q, k, lse, window, ...) -> target
+    budget_mask_fwd(q, k, v, scores, sinks, window, topk, ...) -> (o, lse, rank, cutoff)
+    workspace_size(which, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvpop.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+AGG_SUM, AGG_MAX, AGG_NONE = 0, 1, 2
+CALL_FWD_LSE, CALL_FUTURE_TARGET, CALL_BUDGET_MASK_FWD = 0, 1, 2
+CUTOFF_ALL = 2 ** 31 - 1
+CUTOFF_NONE = -1
+EXPORTS = ("kvpop_attn_fwd_lse", "kvpop_future_target", "kvpop_budget_mask_fwd",
+           "kvpop_workspace_size", "kvpop_status_str", "kvpop_last_error")
+
+_AGG_NAMES = {"sum": AGG_SUM, "max": AGG_MAX, "none": AGG_NONE}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p),
+                ("cu_seqlens_host", ctypes.c_void_p), ("n_docs", ctypes.c_int32)]
+
+
+class KvpopError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libkvpop.so (built in place by attention_target_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_target_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    SP = ctypes.POINTER(Shape)
+    lib.kvpop_attn_fwd_lse.argtypes = [SP, P, P, P, P, P, P]
+    lib.kvpop_attn_fwd_lse.restype = I
+    lib.kvpop_future_target.argtypes = [SP, P, P, P, I, I, I, F, P, P, Z, P]
+    lib.kvpop_future_target.restype = I
+    lib.kvpop_budget_mask_fwd.argtypes = [SP, P, P, P, P, I, I, I, P, P, P, P, P, Z, P]
+    lib.kvpop_budget_mask_fwd.restype = I
+    lib.kvpop_workspace_size.argtypes = [I, SP, I, I, I]
+    lib.kvpop_workspace_size.restype = Z
+    lib.kvpop_status_str.argtypes = [I]
+    lib.kvpop_status_str.restype = ctypes.c_char_p
+    lib.kvpop_last_error.argtypes = []
+    lib.kvpop_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(st: int) -> str:
+    return load().kvpop_status_str(st).decode()
+
+
+def last_error() -> str:
+    return load().kvpop_last_error().decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise KvpopError(st, f"kvpop: {status_str(st)}: {last_error()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+class _Packed:
+    """Host and device copies of the document offsets (kept alive by the caller)."""
+
+    def __init__(self, cu_seqlens, device):
+        if cu_seqlens is None:
+            self.host = self.dev = None
+            self.n_docs = 1
+            return
+        host = torch.as_tensor(cu_seqlens, dtype=torch.int32).detach().to("cpu").contiguous()
+        self.host = host
+        self.dev = host.to(device)
+        self.n_docs = int(host.numel()) - 1
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, packed: _Packed, scale: float) -> Shape:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, S, D]")
+    B, Hq, S, D = q.shape
+    sh = Shape()
+    sh.batch, sh.seqlen, sh.n_q_heads, sh.n_kv_heads, sh.head_dim = B, S, Hq, k.shape[1], D
+    sh.dtype = _dtype_code(q)
+    sh.softmax_scale = float(scale)
+    sh.cu_seqlens = None if packed.dev is None else packed.dev.data_ptr()
+    sh.cu_seqlens_host = None if packed.host is None else packed.host.data_ptr()
+    sh.n_docs = packed.n_docs
+    return sh
+
+
+def _dev(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _require(name: str, t: torch.Tensor, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream_ptr(t: torch.Tensor, stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def workspace_size(which: int, q: torch.Tensor, k: torch.Tensor, cu_seqlens=None, sinks: int = 0,
+                   window: int = 0, topk: int = 0, scale: float = 0.0) -> int:
+    lib = load()
+    packed = _Packed(cu_seqlens, "cpu" if not q.is_cuda else q.device)
+    sh = make_shape(q, k, packed, scale)
+    return int(lib.kvpop_workspace_size(which, ctypes.byref(sh), sinks, window, topk))
+
+
+def attn_fwd_lse(q, k, v, cu_seqlens=None, scale: float = 0.0, need_output: bool = True,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+    """Causal attention forward with per-query LSE (kvpop_attn_fwd_lse)."""
+    lib = load()
+    _require("q", q)
+    _require("k", k, q.dtype)
+    _require("v", v, q.dtype, k.shape)
+    B, Hq, S, D = q.shape
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+    _require("lse", lse, torch.float32, (B, Hq, S))
+    if need_output and out is None:
+        out = torch.empty_like(q)
+    if out is not None:
+        _require("out", out, q.dtype, q.shape)
+    packed = _Packed(cu_seqlens, q.device)
+    sh = make_shape(q, k, packed, scale)
+    _check(lib.kvpop_attn_fwd_lse(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  _dev(out), lse.data_ptr(), _stream_ptr(q, stream)))
+    return out, lse
+
+
+def future_target(q, k, lse, window: int, agg: Union[str, int] = "sum", mean_over_queries: bool = False,
+                  eps: float = 0.0, cu_seqlens=None, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Future-attention target by the transposed pass (kvpop_future_target)."""
+    lib = load()
+    a = _AGG_NAMES[agg] if isinstance(agg, str) else int(agg)
+    _require("q", q)
+    _require("k", k, q.dtype)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _require("lse", lse, torch.float32, (B, Hq, S))
+    Hout = Hq if a == AGG_NONE else Hkv
+    if out is None:
+        out = torch.empty(B, Hout, S, dtype=torch.float32, device=q.device)
+    _require("out", out, torch.float32, (B, Hout, S))
+    packed = _Packed(cu_seqlens, q.device)
+    sh = make_shape(q, k, packed, scale)
+    need = int(lib.kvpop_workspace_size(CALL_FUTURE_TARGET, ctypes.byref(sh), 0, window, 0))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvpop_future_target(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), lse.data_ptr(), int(window),
+                                   a, int(bool(mean_over_queries)), float(eps), out.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream_ptr(q, stream)))
+    return out
+
+
+def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: float = 0.0,
+                    return_rank_cutoff: bool = True, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None):
+    """Fixed-budget sparse attention forward (kvpop_budget_mask_fwd).
+
+    Returns (o, lse, rank, cutoff); rank and cutoff are None unless asked for.
+    """
+    lib = load()
+    _require("q", q)
+    _require("k", k, q.dtype)
+    _require("v", v, q.dtype, k.shape)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _require("scores", scores, torch.float32, (B, Hkv, S))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+    _require("out", out, q.dtype, q.shape)
+    _require("lse", lse, torch.float32, (B, Hq, S))
+    rank = cutoff = None
+    if return_rank_cutoff:
+        rank = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
+        cutoff = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
+    packed = _Packed(None, q.device)
+    sh = make_shape(q, k, packed, scale)
+    need = int(lib.kvpop_workspace_size(CALL_BUDGET_MASK_FWD, ctypes.byref(sh), sinks, window, topk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvpop_budget_mask_fwd(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     scores.data_ptr(), int(sinks), int(window), int(topk), out.data_ptr(),
+                                     lse.data_ptr(), _dev(rank), _dev(cutoff), workspace.data_ptr(),
+                                     workspace.numel(), _stream_ptr(q, stream)))
+    return out, lse, rank, cutoff
+
+
+__all__ = ["load", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+           "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
+           "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
+           "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]
+

@@ -1,0 +1,181 @@
+// C ABI of libkvpop.so (declared in include/kvpop.h): host-side validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Every argument check
+// runs before the first HIP call, so invalid calls never touch the device.
+#include "kvpop.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvpop_status fail(kvpop_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvpop_status ok() {
+  g_last_error.clear();
+  return KVPOP_OK;
+}
+
+// Validates the shape and fills the internal description.
+kvpop_status check_shape(const kvpop_shape *sh, kvpop::ShapeInfo &s) {
+  if (sh == nullptr) return fail(KVPOP_EINVAL, "shape is NULL");
+  if (sh->batch < 1 || sh->seqlen < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1)
+    return fail(KVPOP_EINVAL, "batch, seqlen, n_q_heads and n_kv_heads must be >= 1");
+  if (sh->n_q_heads % sh->n_kv_heads != 0)
+    return fail(KVPOP_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", sh->n_q_heads,
+                sh->n_kv_heads);
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(KVPOP_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", sh->head_dim);
+  if (sh->dtype != KVPOP_BF16 && sh->dtype != KVPOP_F32)
+    return fail(KVPOP_EUNSUPPORTED, "dtype %d is not supported", sh->dtype);
+  if (sh->seqlen > (1 << 24)) return fail(KVPOP_EUNSUPPORTED, "seqlen %d exceeds 2^24", sh->seqlen);
+  const double elems = (double)sh->batch * sh->n_q_heads * sh->seqlen * sh->head_dim;
+  if (elems > 9.0e15) return fail(KVPOP_EUNSUPPORTED, "tensor too large");
+  if ((sh->cu_seqlens == nullptr) != (sh->cu_seqlens_host == nullptr))
+    return fail(KVPOP_EINVAL, "cu_seqlens and cu_seqlens_host must both be set or both be NULL");
+  s.B = sh->batch;
+  s.S = sh->seqlen;
+  s.Hq = sh->n_q_heads;
+  s.Hkv = sh->n_kv_heads;
+  s.D = sh->head_dim;
+  s.dtype = sh->dtype;
+  s.scale = (sh->softmax_scale > 0.f) ? sh->softmax_scale : (float)(1.0 / std::sqrt((double)sh->head_dim));
+  s.cu = sh->cu_seqlens;
+  s.cu_host = sh->cu_seqlens_host;
+  s.n_docs = 1;
+  s.max_doc = sh->seqlen;
+  if (sh->cu_seqlens != nullptr) {
+    if (sh->batch != 1) return fail(KVPOP_EINVAL, "packed sequences (cu_seqlens) need batch == 1");
+    if (sh->n_docs < 1) return fail(KVPOP_EINVAL, "n_docs must be >= 1 with cu_seqlens");
+    const int32_t *c = sh->cu_seqlens_host;
+    if (c[0] != 0) return fail(KVPOP_EINVAL, "cu_seqlens[0] must be 0 (got %d)", c[0]);
+    int mx = 0;
+    for (int m = 0; m < sh->n_docs; ++m) {
+      if (c[m + 1] <= c[m])
+        return fail(KVPOP_EINVAL, "cu_seqlens must rise strictly (index %d: %d -> %d)", m, c[m], c[m + 1]);
+      if (c[m + 1] - c[m] > mx) mx = c[m + 1] - c[m];
+    }
+    if (c[sh->n_docs] != sh->seqlen)
+      return fail(KVPOP_EINVAL, "cu_seqlens[n_docs] = %d but seqlen = %d", c[sh->n_docs], sh->seqlen);
+    s.n_docs = sh->n_docs;
+    s.max_doc = mx;
+  }
+  return KVPOP_OK;
+}
+
+kvpop_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n == 0) {
+    (void)hipGetLastError();
+    return fail(KVPOP_EHIP, "no HIP device available (%s)", hipGetErrorString(e));
+  }
+  return KVPOP_OK;
+}
+
+kvpop_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  (void)hipGetLastError();
+  return fail(KVPOP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvpop_status_str(kvpop_status status) {
+  switch (status) {
+    case KVPOP_OK: return "ok";
+    case KVPOP_EINVAL: return "invalid argument";
+    case KVPOP_EUNSUPPORTED: return "unsupported configuration";
+    case KVPOP_EWORKSPACE: return "workspace too small";
+    case KVPOP_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *kvpop_last_error(void) { return g_last_error.c_str(); }
+
+size_t kvpop_workspace_size(int32_t which, const kvpop_shape *shape, int32_t sinks, int32_t window,
+                            int32_t topk) {
+  kvpop::ShapeInfo s{};
+  if (check_shape(shape, s) != KVPOP_OK) return 0;
+  if (sinks < 0 || window < 0 || topk < 0) return 0;
+  switch (which) {
+    case KVPOP_CALL_FUTURE_TARGET: return kvpop::tgt_workspace_bytes(s);
+    case KVPOP_CALL_BUDGET_MASK_FWD: return kvpop::budget_workspace_bytes(s, sinks, window, topk);
+    default: return 0;
+  }
+}
+
+kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const void *k, const void *v,
+                                void *o, float *lse, void *hip_stream) {
+  kvpop::ShapeInfo s{};
+  kvpop_status st = check_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !v || !lse) return fail(KVPOP_EINVAL, "q, k, v and lse must be non-NULL");
+  if (s.dtype == KVPOP_F32 && s.D != 64)
+    return fail(KVPOP_EUNSUPPORTED, "the fp32 forward supports head_dim 64 only");
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_fwd(s, q, k, v, o, lse, (hipStream_t)hip_stream), "kvpop_attn_fwd_lse launch");
+}
+
+kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const void *k, const float *lse,
+                                 int32_t window, int32_t agg, int32_t mean_over_queries, float eps,
+                                 float *target, void *workspace, size_t ws_bytes, void *hip_stream) {
+  kvpop::ShapeInfo s{};
+  kvpop_status st = check_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !lse || !target) return fail(KVPOP_EINVAL, "q, k, lse and target must be non-NULL");
+  if (window < 0) return fail(KVPOP_EINVAL, "window must be >= 0 (got %d)", window);
+  if (agg != KVPOP_AGG_SUM && agg != KVPOP_AGG_MAX && agg != KVPOP_AGG_NONE)
+    return fail(KVPOP_EINVAL, "agg must be KVPOP_AGG_SUM, _MAX or _NONE (got %d)", agg);
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(KVPOP_EINVAL, "eps must be finite and >= 0");
+  const size_t need = kvpop::tgt_workspace_bytes(s);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_future_target(s, q, k, lse, window, agg, mean_over_queries != 0, eps, target,
+                                              workspace, (hipStream_t)hip_stream),
+                  "kvpop_future_target launch");
+}
+
+kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, const void *k, const void *v,
+                                   const float *scores, int32_t sinks, int32_t window, int32_t topk, void *o,
+                                   float *lse, int32_t *rank_out, int32_t *cutoff_out, void *workspace,
+                                   size_t ws_bytes, void *hip_stream) {
+  kvpop::ShapeInfo s{};
+  kvpop_status st = check_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !v || !scores || !o || !lse)
+    return fail(KVPOP_EINVAL, "q, k, v, scores, o and lse must be non-NULL");
+  if (sinks < 0 || window < 0 || topk < 0)
+    return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
+  if (s.cu != nullptr) return fail(KVPOP_EUNSUPPORTED, "the budget mask does not support packed sequences");
+  if (s.dtype == KVPOP_F32 && s.D != 64)
+    return fail(KVPOP_EUNSUPPORTED, "the fp32 budget forward supports head_dim 64 only");
+  const size_t need = kvpop::budget_workspace_bytes(s, sinks, window, topk);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_budget(s, q, k, v, scores, sinks, window, topk, o, lse, rank_out, cutoff_out,
+                                       workspace, (hipStream_t)hip_stream),
+                  "kvpop_budget_mask_fwd launch");
+}
+
+}  // extern "C"

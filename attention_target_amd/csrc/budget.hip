@@ -1,0 +1,398 @@
+// Fixed-budget sparse attention for gfx950 (kvpop_budget_mask_fwd).
+//
+// KVpop paper, Section 3: every KV head keeps s sink tokens (the first
+// positions), a protected window of the w most recent tokens, and the top-k
+// of the eligible tokens E_d = [s, d-w] (Section 3.1, Eq. 4) ranked by static
+// priorities.  Section 3.2 ("Running top-k sparse attention"): sort once by
+// priority, and the retained long-range keys of query d are exactly the
+// eligible tokens whose rank is at most c_d, the rank of the k-th best
+// eligible token.  The pages compute c_d with a sequential Fenwick-tree sweep;
+// here every c_d is an independent query on a wavelet matrix over the ranks
+// (k-th smallest value in the prefix [s, d-w]), which gives the same integers
+// for all d in parallel.
+//
+// Pipeline (all on the caller's stream):
+//   1. keys:    64-bit sort key (descending score, ascending index) per token;
+//   2. sort:    2048-key chunks sorted in LDS (bitonic);
+//   3. rank:    rank(t) = sum over chunks of the number of smaller keys;
+//   4. wavelet: one workgroup per (batch, KV head) builds the log2(S) levels
+//               (bitvectors + per-word prefix counts) by stable partitions;
+//   5. cutoff:  c_d for every d (KVPOP_CUTOFF_ALL when |E_d| < k, _NONE when
+//               k = 0);
+//   6. lists:   per query block [d0, d1] the ascending union of the keys any
+//               of its queries may keep: [0, s) below the window, the eligible
+//               tokens of [s, d0-w] with rank <= c_{d0}, and (d0-w, d1];
+//   7. forward: attention over the listed keys with per-element membership
+//               t <= d and (t < s or t > d-w or rank(t) <= c_d).
+#include "attn_fwd.h"
+#include "launch.h"
+
+namespace kvpop {
+
+constexpr int RANK_CH = 2048;
+constexpr int CUT_ALL = 2147483647;
+constexpr int CUT_NONE = -1;
+
+struct BudgetLayout {
+  size_t keys, sorted, rank, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, total;
+  int S_pad, nchunks, L, nw1, nqb, QB, cap;
+};
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int topk) {
+  BudgetLayout lo{};
+  const size_t BH = (size_t)s.B * s.Hkv;
+  lo.nchunks = (s.S + RANK_CH - 1) / RANK_CH;
+  lo.S_pad = lo.nchunks * RANK_CH;
+  lo.L = 1;
+  while ((1ll << lo.L) < (long long)s.S) ++lo.L;
+  lo.nw1 = (s.S + 31) / 32 + 1;
+  const int HG = fwd_heads_per_block(s.Hq / s.Hkv);
+  lo.QB = 32 * (4 / HG);
+  lo.nqb = (s.S + lo.QB - 1) / lo.QB;
+  long long cap = (long long)sinks + topk + window + lo.QB;
+  if (cap > s.S) cap = s.S;
+  lo.cap = (int)((cap + 3) & ~3ll);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = al256(off + bytes);
+    return o;
+  };
+  lo.keys = take(BH * lo.S_pad * 8);
+  lo.sorted = take(BH * lo.S_pad * 8);
+  lo.rank = take(BH * s.S * 4);
+  lo.cutoff = take(BH * s.S * 4);
+  lo.arr0 = take(BH * s.S * 4);
+  lo.arr1 = take(BH * s.S * 4);
+  lo.bits = take(BH * lo.L * lo.nw1 * 4);
+  lo.prefix = take(BH * lo.L * lo.nw1 * 4);
+  lo.zeros = take(BH * lo.L * 4);
+  lo.lists = take(BH * lo.nqb * (size_t)lo.cap * 4);
+  lo.lens = take(BH * lo.nqb * 4);
+  lo.total = off;
+  return lo;
+}
+
+size_t budget_workspace_bytes(const ShapeInfo &s, int sinks, int window, int topk) {
+  return budget_layout(s, sinks, window, topk).total;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Sort key: ascending order = descending score, then ascending index.  -0.0
+// is folded into +0.0 and NaN into -inf before the order-preserving map.
+__device__ __forceinline__ uint64_t score_key(float sc, int t) {
+  if (sc != sc) sc = -INFINITY;
+  if (sc == 0.f) sc = 0.f;
+  const uint32_t u = __float_as_uint(sc);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)(~ord) << 32) | (uint32_t)t;
+}
+
+__global__ void __launch_bounds__(256) budget_keys(const float *scores, uint64_t *keys, int S, int S_pad) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= S_pad) return;
+  keys[bh * S_pad + t] = (t < S) ? score_key(scores[bh * S + t], t) : ~0ull;
+}
+
+__global__ void __launch_bounds__(256) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad, int nchunks) {
+  __shared__ uint64_t sh[RANK_CH];
+  const size_t base = (size_t)blockIdx.y * S_pad + (size_t)blockIdx.x * RANK_CH;
+  for (int i = threadIdx.x; i < RANK_CH; i += 256) sh[i] = keys[base + i];
+  __syncthreads();
+  for (int k = 2; k <= RANK_CH; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < RANK_CH; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const uint64_t a = sh[i], b = sh[ixj];
+          if ((a > b) == up) {
+            sh[i] = b;
+            sh[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < RANK_CH; i += 256) sorted[base + i] = sh[i];
+}
+
+__global__ void __launch_bounds__(256) budget_rank(const uint64_t *keys, const uint64_t *sorted, int *rank,
+                                                   int S, int S_pad, int nchunks) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= S) return;
+  const uint64_t key = keys[bh * S_pad + t];
+  int cnt = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const uint64_t *a = sorted + bh * S_pad + (size_t)c * RANK_CH;
+    int lo = 0, hi = RANK_CH;  // first index with a[i] >= key
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a[mid] < key) lo = mid + 1; else hi = mid;
+    }
+    cnt += lo;
+  }
+  rank[bh * S + t] = cnt;
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads).
+__device__ __forceinline__ int block_excl_scan_1024(int x, int *sh_waves, int &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh_waves[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int v = sh_waves[w];
+    if (w < wave) before += v;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - x;
+}
+
+struct WaveletParams {
+  const int *rank;
+  int *arr0, *arr1;
+  uint32_t *bits;
+  int *prefix, *zeros;
+  int S, sinks, L, nw1;
+};
+
+// One workgroup (1024 threads) per (batch, KV head): levels from the top bit
+// down; each level stores the bit of every element of the current
+// arrangement and then partitions it stably (zeros first).
+__global__ void __launch_bounds__(1024) budget_wavelet_build(const WaveletParams p) {
+  __shared__ int sh_waves[16];
+  const size_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_e = p.S - p.sinks;
+  if (n_e <= 0) return;
+  int *cur = p.arr0 + bh * p.S;
+  int *nxt = p.arr1 + bh * p.S;
+  for (int i = tid; i < n_e; i += 1024) cur[i] = p.rank[bh * p.S + p.sinks + i];
+  __threadfence();
+  __syncthreads();
+  const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
+  for (int lvl = p.L - 1; lvl >= 0; --lvl) {
+    uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+    int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+    for (int base = 0; base < 32 * p.nw1; base += 1024) {
+      const int i = base + tid;
+      const int bit = (i < n_e) ? ((cur[i] >> lvl) & 1) : 0;
+      const uint64_t m = __ballot(bit);
+      const int w0 = (base + 64 * wave) / 32;
+      if (lane == 0 && w0 < p.nw1) bl[w0] = (uint32_t)m;
+      if (lane == 0 && w0 + 1 < p.nw1) bl[w0 + 1] = (uint32_t)(m >> 32);
+    }
+    __threadfence();
+    __syncthreads();
+    int local = 0;
+    for (int q = 0; q < wpt; ++q) {
+      const int w = tid * wpt + q;
+      if (w < p.nw1) local += __popc(bl[w]);
+    }
+    int ones;
+    int run = block_excl_scan_1024(local, sh_waves, ones);
+    for (int q = 0; q < wpt; ++q) {
+      const int w = tid * wpt + q;
+      if (w < p.nw1) {
+        pl[w] = run;
+        run += __popc(bl[w]);
+      }
+    }
+    const int Z = n_e - ones;
+    if (tid == 0) p.zeros[bh * p.L + lvl] = Z;
+    __threadfence();
+    __syncthreads();
+    for (int i = tid; i < n_e; i += 1024) {
+      const int v = cur[i];
+      const int w = i >> 5;
+      const int before = pl[w] + __popc(bl[w] & ((1u << (i & 31)) - 1u));
+      const int pos = ((v >> lvl) & 1) ? Z + before : i - before;
+      if (pos >= 0 && pos < n_e) nxt[pos] = v;
+    }
+    __threadfence();
+    __syncthreads();
+    int *tmp = cur;
+    cur = nxt;
+    nxt = tmp;
+  }
+}
+
+__global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int window, int topk, int *cutoff) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (d >= p.S) return;
+  const long long m_e = (long long)d - window - p.sinks + 1;  // |E_d|
+  int res;
+  if (topk <= 0) {
+    res = CUT_NONE;
+  } else if (m_e < topk) {
+    res = CUT_ALL;
+  } else {
+    const int n_e = p.S - p.sinks;
+    int l = 0, r = (int)m_e, kk = topk - 1, val = 0;
+    for (int lvl = p.L - 1; lvl >= 0; --lvl) {
+      const uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+      const int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+      const int ol = pl[l >> 5] + __popc(bl[l >> 5] & ((1u << (l & 31)) - 1u));
+      const int orr = pl[r >> 5] + __popc(bl[r >> 5] & ((1u << (r & 31)) - 1u));
+      const int zin = (r - l) - (orr - ol);
+      if (kk < zin) {
+        l -= ol;
+        r -= orr;
+      } else {
+        kk -= zin;
+        const int Z = p.zeros[bh * p.L + lvl];
+        l = Z + ol;
+        r = Z + orr;
+        val |= 1 << lvl;
+      }
+      l = min(max(l, 0), n_e);  // stays in range for a well-formed matrix; guards the reads otherwise
+      r = min(max(r, l), n_e);
+    }
+    res = val;
+  }
+  cutoff[bh * p.S + d] = res;
+}
+
+struct ListParams {
+  const int *rank, *cutoff;
+  int *lists, *lens;
+  int S, sinks, window, QB, nqb, cap;
+};
+
+__global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
+  __shared__ int sh_w[4];
+  const int qb = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d0 = qb * p.QB, d1 = min(p.S - 1, d0 + p.QB - 1);
+  const int c0 = p.cutoff[bh * p.S + d0];
+  int *list = p.lists + (bh * p.nqb + qb) * (size_t)p.cap;
+  const int a_end = max(0, min(min(p.sinks, d0 - p.window + 1), d1 + 1));
+  for (int i = tid; i < a_end && i < p.cap; i += 256) list[i] = i;
+  int off = a_end;
+  const int b_hi = d0 - p.window;
+  for (int base = p.sinks; base <= b_hi; base += 256) {
+    const int t = base + tid;
+    const bool f = (t <= b_hi) && (p.rank[bh * p.S + t] <= c0);
+    const uint64_t m = __ballot(f);
+    if (lane == 0) sh_w[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) before += sh_w[w];
+      tot += sh_w[w];
+    }
+    const int slot = off + before + __popcll(m & lanemask_lt(lane));
+    if (f && slot < p.cap) list[slot] = t;
+    off += tot;
+    __syncthreads();
+  }
+  const int c_lo = max(0, d0 - p.window + 1);
+  const int n_c = d1 - c_lo + 1;
+  for (int i = tid; i < n_c && off + i < p.cap; i += 256) list[off + i] = c_lo + i;
+  if (tid == 0) p.lens[bh * p.nqb + qb] = min(off + n_c, p.cap);
+}
+
+template <typename T, int D>
+static hipError_t run_sparse(const FwdParams &fp, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, fp);
+  return hipGetLastError();
+}
+
+hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const void *v,
+                         const float *scores, int sinks, int window, int topk, void *o, float *lse,
+                         int *rank_out, int *cutoff_out, void *ws, hipStream_t st) {
+  const BudgetLayout lo = budget_layout(s, sinks, window, topk);
+  char *w = reinterpret_cast<char *>(ws);
+  const int BH = s.B * s.Hkv;
+  uint64_t *keys = reinterpret_cast<uint64_t *>(w + lo.keys);
+  uint64_t *sorted = reinterpret_cast<uint64_t *>(w + lo.sorted);
+  int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
+  int *cutoff = cutoff_out ? cutoff_out : reinterpret_cast<int *>(w + lo.cutoff);
+
+  hipLaunchKernelGGL(budget_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, scores, keys, s.S, lo.S_pad);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(256), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_rank, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, s.S, lo.S_pad, lo.nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  WaveletParams wp{};
+  wp.rank = rank;
+  wp.arr0 = reinterpret_cast<int *>(w + lo.arr0);
+  wp.arr1 = reinterpret_cast<int *>(w + lo.arr1);
+  wp.bits = reinterpret_cast<uint32_t *>(w + lo.bits);
+  wp.prefix = reinterpret_cast<int *>(w + lo.prefix);
+  wp.zeros = reinterpret_cast<int *>(w + lo.zeros);
+  wp.S = s.S;
+  wp.sinks = sinks;
+  wp.L = lo.L;
+  wp.nw1 = lo.nw1;
+  if (topk > 0 && s.S - sinks > 0)
+    hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
+  hipLaunchKernelGGL(budget_cutoffs, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, wp, window, topk, cutoff);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  ListParams lp{};
+  lp.rank = rank;
+  lp.cutoff = cutoff;
+  lp.lists = reinterpret_cast<int *>(w + lo.lists);
+  lp.lens = reinterpret_cast<int *>(w + lo.lens);
+  lp.S = s.S;
+  lp.sinks = sinks;
+  lp.window = window;
+  lp.QB = lo.QB;
+  lp.nqb = lo.nqb;
+  lp.cap = lo.cap;
+  hipLaunchKernelGGL(budget_lists, dim3(lo.nqb, BH), dim3(256), 0, st, lp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  FwdParams fp{};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.o = o;
+  fp.lse = lse;
+  fp.B = s.B;
+  fp.S = s.S;
+  fp.Hq = s.Hq;
+  fp.Hkv = s.Hkv;
+  fp.G = s.Hq / s.Hkv;
+  fp.HG = fwd_heads_per_block(fp.G);
+  fp.scale_log2 = s.scale * kLog2e;
+  fp.cu = nullptr;
+  fp.n_docs = 1;
+  fp.lists = lp.lists;
+  fp.list_len = lp.lens;
+  fp.rank = rank;
+  fp.cutoff = cutoff;
+  fp.list_cap = lo.cap;
+  fp.sinks = sinks;
+  fp.window = window;
+  const int grid = lo.nqb * s.B * s.Hkv * (fp.G / fp.HG);
+  if (s.dtype == 0 && s.D == 128) return run_sparse<bf16, 128>(fp, grid, st);
+  if (s.dtype == 0 && s.D == 64) return run_sparse<bf16, 64>(fp, grid, st);
+  if (s.dtype == 1 && s.D == 64) return run_sparse<float, 64>(fp, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvpop

@@ -1,0 +1,357 @@
+// Transposed-attention future target for gfx950.
+//
+// KVpop paper, Section 3.2 ("Transposed-attention target computation",
+// Eq. 8): the future mass of key t is a reduction over the column t of the
+// attention matrix, ln sum_{d >= t+w} exp(s_{d,t} - L_d), evaluated with keys
+// in the role of queries.  Section 3.1 (Eqs. 2-3) turns the per-query-head
+// masses into the target (mean over the N_t future queries, epsilon, max or
+// sum over the query heads of a KV head).
+//
+// Work decomposition
+//  * A block is (batch row, KV head, document, key tile of 256 keys, query
+//    chunk of DT queries).  Its four waves each keep 64 keys of K resident in
+//    registers (the MFMA A operand) for the whole block.
+//  * Query tiles of 32 positions stream through double-buffered, swizzled
+//    LDS together with -L_d*log2(e); for every query head of the group each
+//    wave computes S^T (64 keys x 32 queries) with MFMA and, per element,
+//    p = exp2(s * scale*log2e - L*log2e) added into per-lane fp32 sums.  No
+//    running max is needed: with the dense normaliser s_{d,t} <= L_d.
+//  * The masks d >= t + w and "inside the document" are applied only on the
+//    sub-tiles that cross them.
+//  * At the end each wave reduce-scatters its 32 per-lane sums (31 shuffles)
+//    and writes one partial per key and query chunk into the workspace; a
+//    second small kernel adds the chunks in a fixed order, applies the mean,
+//    epsilon and the aggregation over query heads, and takes the log.  There
+//    are no atomics, so results are bitwise reproducible.
+//  * Blocks are ordered (batch, KV head, document, chunk descending, key tile)
+//    and dealt out so that each XCD (one L2) receives a contiguous range:
+//    concurrently running blocks of an XCD share the same query chunk.
+#include "common.h"
+#include "launch.h"
+
+namespace kvpop {
+
+constexpr int TGT_KT = 256;  // keys per block: 4 waves x 64
+
+struct TgtParams {
+  const void *q, *k;
+  const float *lse;
+  float *part;
+  int B, S, Hq, Hkv, G, window;
+  float scale_log2;
+  const int *cu;
+  int n_docs;
+  int DT, nch_max, blocks_per_seq, total_blocks, Hp;
+};
+
+// Number of key tiles of a document of length n that meet query chunk j.
+__host__ __device__ __forceinline__ int tgt_tiles_in_chunk(int n, int j, int DT, int w) {
+  const int qend = min(n, (j + 1) * DT) - 1;
+  if (qend - w < 0) return 0;
+  return min((n + TGT_KT - 1) / TGT_KT, (qend - w) / TGT_KT + 1);
+}
+__host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w) {
+  const int nch = (n + DT - 1) / DT;
+  int c = 0;
+  for (int j = 0; j < nch; ++j) c += tgt_tiles_in_chunk(n, j, DT, w);
+  return c;
+}
+
+template <typename T, int D, bool SUM_HEADS>
+__global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
+  using QTile = SwizzledTile<T, D>;
+  constexpr int NJ = D / 16;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int CPR = D / EPC;
+  constexpr int Q_PER_THREAD = 32 * CPR / 256;
+  static_assert(32 * CPR % 256 == 0, "Q tile must split over 256 threads");
+  constexpr int QBYTES = 32 * D * (int)sizeof(T);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+  __shared__ __align__(16) char q_lds[2][QBYTES];
+  __shared__ float nl_lds[2][32];
+
+  // ---- which block ----
+  const int per_xcd = (p.total_blocks + 7) / 8;
+  const int v = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  if (v >= p.total_blocks) return;
+  const int bh = v / p.blocks_per_seq;
+  int r = v % p.blocks_per_seq;
+  const int b = bh / p.Hkv, h = bh % p.Hkv;
+  int dstart = 0, n = p.S;
+  bool found = false;
+  for (int m = 0; m < p.n_docs; ++m) {
+    if (p.cu != nullptr) {
+      dstart = p.cu[m];
+      n = p.cu[m + 1] - dstart;
+    }
+    const int cnt = tgt_blocks_in_doc(n, p.DT, p.window);
+    if (r < cnt) {
+      found = true;
+      break;
+    }
+    r -= cnt;
+  }
+  if (!found || n <= 0 || dstart < 0 || dstart + n > p.S) return;  // host and device offsets disagree
+  const int nch = (n + p.DT - 1) / p.DT;
+  if (nch > p.nch_max) return;
+  int j = nch - 1;
+  for (; j >= 0; --j) {
+    const int nt = tgt_tiles_in_chunk(n, j, p.DT, p.window);
+    if (r < nt) break;
+    r -= nt;
+  }
+  if (j < 0) return;
+  const int t0 = r * TGT_KT;  // doc-local first key of the block
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int tw = t0 + 64 * wave;  // doc-local first key of this wave
+  const int w = p.window;
+
+  // ---- resident K fragments (A operand) ----
+  const T *kbase = reinterpret_cast<const T *>(p.k) + ((size_t)b * p.Hkv + h) * (size_t)p.S * D;
+  Frag<T> kf[2][NJ];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int key = min(tw + 32 * rb + col, n - 1);
+    const T *kr = kbase + (size_t)(dstart + key) * D + 8 * hf;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) load_frag(kf[rb][jj], kr + 16 * jj);
+  }
+
+  // ---- query sub-tiles of this chunk ----
+  const int cq0 = j * p.DT, cq1 = min(n, (j + 1) * p.DT);
+  const int qs = max(cq0, t0 + w);
+  const int qs_al = cq0 + ((qs - cq0) & ~31);
+  const int n_sub = (cq1 - qs_al + 31) / 32;
+  const int n_it = p.G * n_sub;
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  u32x4 qreg[Q_PER_THREAD];
+  float nlreg = 0.f;
+
+  auto q_of = [&](int it, int &gg, int &q0) {
+    gg = it / n_sub;
+    q0 = qs_al + 32 * (it % n_sub);
+  };
+  auto prefetch = [&](int it) {
+    int gg, q0;
+    q_of(it, gg, q0);
+    const int g = h * p.G + gg;
+    const T *qb = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + g) * (size_t)p.S * D;
+#pragma unroll
+    for (int c = 0; c < Q_PER_THREAD; ++c) {
+      const int li = tid + 256 * c;
+      const int rr = li / CPR, ch = li % CPR;
+      const int qrow = dstart + min(q0 + rr, n - 1);
+      qreg[c] = *reinterpret_cast<const u32x4 *>(qb + (size_t)qrow * D + ch * EPC);
+    }
+    if (tid < 32) {
+      const int qrow = dstart + min(q0 + tid, n - 1);
+      nlreg = -p.lse[((size_t)b * p.Hq + g) * p.S + qrow] * kLog2e;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < Q_PER_THREAD; ++c) {
+      const int li = tid + 256 * c;
+      const int rr = li / CPR, ch = li % CPR;
+      *reinterpret_cast<u32x4 *>(q_lds[buf] + QTile::off(rr, ch)) = qreg[c];
+    }
+    if (tid < 32) nl_lds[buf][tid] = nlreg;
+  };
+  auto write_partial = [&](int hp) {
+    // reduce-scatter the 32 per-lane sums across the 32 lanes of each half
+    float vals[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      vals[i] = acc[0][i];
+      vals[16 + i] = acc[1][i];
+    }
+#pragma unroll
+    for (int st = 0; st < 5; ++st) {
+      const int m = 16 >> st;
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < m; ++i) {
+        const float send = upper ? vals[i] : vals[i + m];
+        const float keep = upper ? vals[i + m] : vals[i];
+        vals[i] = keep + __shfl_xor(send, m);
+      }
+    }
+    const int rsel = lane & 31;
+    const int kk = 32 * (rsel / 16) + c_row(rsel % 16, hf);
+    const int key = tw + kk;
+    if (key < n) p.part[(((size_t)b * p.Hp + hp) * p.nch_max + j) * p.S + dstart + key] = vals[0];
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+  };
+
+  const float c = p.scale_log2;
+  prefetch(0);
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    store(buf);
+    __syncthreads();
+    if (it + 1 < n_it) prefetch(it + 1);
+
+    int gg, q0;
+    q_of(it, gg, q0);
+    const bool any = (q0 + 31 >= tw + w) && (tw < n);
+    if (any) {
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        Frag<T> bq;
+        QTile::read(bq, q_lds[buf], col, 16 * jj + 8 * hf);
+        mma(s[0], kf[0][jj], bq);
+        mma(s[1], kf[1][jj], bq);
+      }
+      const float nl = nl_lds[buf][col];
+      const bool interior = (q0 >= tw + 63 + w) && (q0 + 31 < n) && (tw + 63 < n);
+      if (interior) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[rb][i] += fast_exp2(__builtin_fmaf(s[rb][i], c, nl));
+      } else {
+        const int d = q0 + col;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int t = tw + 32 * rb + c_row(i, hf);
+            const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, nl));
+            acc[rb][i] += (d >= t + w && d < n && t < n) ? pv : 0.f;
+          }
+      }
+    }
+    if constexpr (!SUM_HEADS) {
+      if ((it + 1) % n_sub == 0) write_partial(h * p.G + gg);
+    }
+  }
+  if constexpr (SUM_HEADS) write_partial(h);
+}
+
+struct FinParams {
+  const float *part;
+  float *out;
+  int B, S, Hq, Hkv, G, window, DT, nch_max, Hp, Hout, agg, mean;
+  float eps;
+  const int *cu;
+  int n_docs;
+};
+
+__global__ void __launch_bounds__(256) future_target_finalize(const FinParams p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.S) return;
+  const int ho = blockIdx.y, b = blockIdx.z;
+  const Doc dd = find_doc(p.cu, p.n_docs, p.S, t);
+  const int n = dd.end - dd.start, pos = t - dd.start;
+  const int N = max(0, n - pos - p.window);
+  const int fq = (pos / TGT_KT) * TGT_KT + p.window;
+  const int nch = (n + p.DT - 1) / p.DT;
+  const int jlo = (fq <= n - 1) ? fq / p.DT : nch;
+  const float scale = p.mean ? (N > 0 ? 1.f / (float)N : 0.f) : 1.f;
+  auto mass = [&](int hp) {
+    float s = 0.f;
+    for (int jj = jlo; jj < nch; ++jj) s += p.part[(((size_t)b * p.Hp + hp) * p.nch_max + jj) * p.S + t];
+    return s * scale;
+  };
+  float y;
+  if (p.agg == 0) {
+    y = logf(mass(ho) + p.eps);
+  } else if (p.agg == 1) {
+    y = -INFINITY;
+    for (int gg = 0; gg < p.G; ++gg) y = fmaxf(y, logf(mass(ho * p.G + gg) + p.eps));
+  } else {
+    y = logf(mass(ho) + p.eps);
+  }
+  p.out[((size_t)b * p.Hout + ho) * p.S + t] = y;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+int tgt_chunk(int max_doc) {
+  if (max_doc <= 4096) return 256;
+  if (max_doc <= 8192) return 512;
+  return 1024;
+}
+
+size_t tgt_workspace_bytes(const ShapeInfo &s) {
+  const int DT = tgt_chunk(s.max_doc);
+  const size_t nch_max = (size_t)((s.max_doc + DT - 1) / DT);
+  return (size_t)s.B * s.Hq * nch_max * s.S * sizeof(float);
+}
+
+template <typename T, int D, bool SUM>
+static hipError_t launch_tgt(const TgtParams &tp, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((future_target_kernel<T, D, SUM>), dim3(grid), dim3(256), 0, st, tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k, const float *lse,
+                                int window, int agg, int mean, float eps, float *target,
+                                void *ws, hipStream_t st) {
+  TgtParams tp{};
+  tp.q = q;
+  tp.k = k;
+  tp.lse = lse;
+  tp.part = reinterpret_cast<float *>(ws);
+  tp.B = s.B;
+  tp.S = s.S;
+  tp.Hq = s.Hq;
+  tp.Hkv = s.Hkv;
+  tp.G = s.Hq / s.Hkv;
+  tp.window = window;
+  tp.scale_log2 = s.scale * kLog2e;
+  tp.cu = s.cu;
+  tp.n_docs = s.n_docs;
+  tp.DT = tgt_chunk(s.max_doc);
+  tp.nch_max = (s.max_doc + tp.DT - 1) / tp.DT;
+  int per_seq = 0;
+  if (s.cu_host != nullptr) {
+    for (int m = 0; m < s.n_docs; ++m)
+      per_seq += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], tp.DT, window);
+  } else {
+    per_seq = tgt_blocks_in_doc(s.S, tp.DT, window);
+  }
+  tp.blocks_per_seq = per_seq;
+  tp.total_blocks = per_seq * s.B * s.Hkv;
+  const bool sum = (agg == 0);
+  tp.Hp = sum ? s.Hkv : s.Hq;
+  hipError_t e = hipSuccess;
+  if (tp.total_blocks > 0) {
+    const int grid = 8 * ((tp.total_blocks + 7) / 8);
+    if (s.dtype == 0 && s.D == 128) e = sum ? launch_tgt<bf16, 128, true>(tp, grid, st) : launch_tgt<bf16, 128, false>(tp, grid, st);
+    else if (s.dtype == 0 && s.D == 64) e = sum ? launch_tgt<bf16, 64, true>(tp, grid, st) : launch_tgt<bf16, 64, false>(tp, grid, st);
+    else if (s.dtype == 1 && s.D == 64) e = sum ? launch_tgt<float, 64, true>(tp, grid, st) : launch_tgt<float, 64, false>(tp, grid, st);
+    else if (s.dtype == 1 && s.D == 128) e = sum ? launch_tgt<float, 128, true>(tp, grid, st) : launch_tgt<float, 128, false>(tp, grid, st);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+  }
+  FinParams fp{};
+  fp.part = tp.part;
+  fp.out = target;
+  fp.B = s.B;
+  fp.S = s.S;
+  fp.Hq = s.Hq;
+  fp.Hkv = s.Hkv;
+  fp.G = tp.G;
+  fp.window = window;
+  fp.DT = tp.DT;
+  fp.nch_max = tp.nch_max;
+  fp.Hp = tp.Hp;
+  fp.Hout = (agg == 2) ? s.Hq : s.Hkv;
+  fp.agg = agg;
+  fp.mean = mean;
+  fp.eps = eps;
+  fp.cu = s.cu;
+  fp.n_docs = s.n_docs;
+  hipLaunchKernelGGL(future_target_finalize, dim3((s.S + 255) / 256, fp.Hout, s.B), dim3(256), 0, st, fp);
+  return hipGetLastError();
+}
+
+}  // namespace kvpop

@@ -1,0 +1,35 @@
+// Host-side launchers of libkvpop (internal; the public ABI is include/kvpop.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kvpop {
+
+// A validated problem description (see kvpop_shape in include/kvpop.h).
+struct ShapeInfo {
+  int B, S, Hq, Hkv, D, dtype;  // dtype: 0 = bf16, 1 = fp32
+  float scale;                  // softmax scale (already defaulted)
+  const int *cu;                // device offsets or nullptr
+  const int *cu_host;           // host offsets or nullptr
+  int n_docs;                   // documents per sequence (1 without offsets)
+  int max_doc;                  // longest document
+};
+
+hipError_t launch_fwd(const ShapeInfo &s, const void *q, const void *k, const void *v, void *o,
+                      float *lse, hipStream_t st);
+
+size_t tgt_workspace_bytes(const ShapeInfo &s);
+hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k, const float *lse,
+                                int window, int agg, int mean, float eps, float *target, void *ws,
+                                hipStream_t st);
+
+size_t budget_workspace_bytes(const ShapeInfo &s, int sinks, int window, int topk);
+hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const void *v,
+                         const float *scores, int sinks, int window, int topk, void *o, float *lse,
+                         int *rank_out, int *cutoff_out, void *ws, hipStream_t st);
+
+// Query heads of one GQA group handled by one forward workgroup.
+inline int fwd_heads_per_block(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
+}  // namespace kvpop

@@ -1,0 +1,186 @@
+"""Benchmark of the KVpop future-attention target path on one MI355X.
+
+One step = one pass of the hot path over the full Qwen3-4B attention stack of
+one training step: for each of 36 layers (B=2, S=16384, 32 query heads / 8 KV
+heads, head_dim 128, bf16, w=128) the causal forward with LSE, then the
+transposed target pass that produces ln(future mass) for all 2*8*16384 keys.
+Inputs for all layers are generated once and stay resident in HBM.
+
+Prints one JSON line.  `value` is target keys per second of the whole step
+(forward + target); per-kernel timings, TFLOP/s and the fraction of the bf16
+dense MFMA peak are reported alongside, with the fp64 CPU oracle timed on a
+bounded sample of the same workload as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "future-attention target keys/s + TFLOP/s (% bf16 MFMA peak) at S=16384"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def target_pairs(lengths, w):
+    """(d, t) pairs with d >= t + w inside each document."""
+    return sum(max(0, n - w) * (max(0, n - w) + 1) // 2 for n in lengths)
+
+
+def causal_pairs(lengths):
+    return sum(n * (n + 1) // 2 for n in lengths)
+
+
+def cpu_baseline(q, k, v, window, budget_s: float = 20.0):
+    """Time the fp64 oracle (untuned) on one batch row and one KV-head group
+    (4 query heads, all 16384 queries and keys) of layer 0: dense forward with
+    LSE, column sums and the SUM target for 16384 keys."""
+    import numpy as np
+    from oracle import dense
+    G = q.shape[1] // k.shape[1]
+    qs = q[0:1, 0:G].to("cpu")
+    ks = k[0:1, 0:1].to("cpu")
+    vs = v[0:1, 0:1].to("cpu")
+    t0 = time.perf_counter()
+    r = dense.reference(qs, ks, vs, window=window)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["lse"]).all()
+    S = q.shape[2]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": S / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0, batch row 0, KV head 0 with its {G} query heads: fp64 dense forward+LSE "
+                      f"and target for {S} keys at S={S} ({dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no collectives: "
+              f"each GPU would run its own (batch, KV head) share independently.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import attention_target_amd as kv
+    import synth
+    kv.load()
+    dev = torch.device("cuda:0")
+    spec = synth.WORKLOADS["stack36"]
+    L, B, S, Hq, Hkv, D, w = spec.layers, spec.batch, spec.seqlen, spec.n_q_heads, spec.n_kv_heads, \
+        spec.head_dim, spec.window
+    layers = []
+    for layer in range(L):
+        t = synth.make_workload("stack36", layer=layer, device=dev)
+        layers.append({
+            "q": t["q"], "k": t["k"], "v": t["v"],
+            "o": torch.empty_like(t["q"]),
+            "lse": torch.empty(B, Hq, S, dtype=torch.float32, device=dev),
+            "tgt": torch.empty(B, Hkv, S, dtype=torch.float32, device=dev),
+        })
+    ws = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, layers[0]["q"], layers[0]["k"], window=w),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, ly in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            kv.attn_fwd_lse(ly["q"], ly["k"], ly["v"], out=ly["o"], lse=ly["lse"], stream=stream)
+            if events is not None:
+                events[i][1].record(stream)
+            kv.future_target(ly["q"], ly["k"], ly["lse"], w, out=ly["tgt"], workspace=ws, stream=stream)
+            if events is not None:
+                events[i][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel durations (HIP events on the launch stream), separate pass
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
+    fwd_ms, tgt_ms = [], []
+    for _ in range(max(1, min(args.steps, 3))):
+        step(ev)
+        torch.cuda.synchronize()
+        for e in ev:
+            fwd_ms.append(e[0].elapsed_time(e[1]))
+            tgt_ms.append(e[1].elapsed_time(e[2]))
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    tgt_avg = sum(tgt_ms) / len(tgt_ms)
+
+    lengths = [S]
+    keys_per_step = L * B * Hkv * S
+    tgt_flop = 2 * D * Hq * B * target_pairs(lengths, w)        # QK^T only, pairs with d >= t + w
+    fwd_flop = 4 * D * Hq * B * causal_pairs(lengths)           # QK^T and PV over causal pairs
+    tgt_tflops = tgt_flop / (tgt_avg * 1e-3) / 1e12
+    fwd_tflops = fwd_flop / (fwd_avg * 1e-3) / 1e12
+    step_tflops = L * (tgt_flop + fwd_flop) / (ms_per_step * 1e-3) / 1e12
+
+    def roof(name, flop, ms, tflops):
+        return {"kernel": name, "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flop_per_launch": flop, "avg_launch_ms": round(ms, 4)}
+
+    r_tgt = roof("future_target (kvpop_future_target)", tgt_flop, tgt_avg, tgt_tflops)
+    r_fwd = roof("attn_fwd (kvpop_attn_fwd_lse)", fwd_flop, fwd_avg, fwd_tflops)
+    dominant = r_fwd if fwd_avg >= tgt_avg else r_tgt
+
+    out = {
+        "metric": METRIC,
+        "value": round(keys_per_step / (ms_per_step * 1e-3), 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V with 1% heavy-hitter keys; no weights or datasets)",
+        "config": {"workload": "stack36: 36 layers x (B=2, S=16384, 32q/8kv heads, head_dim 128), w=128; "
+                               "per layer causal forward+LSE then transposed target (SUM over the GQA group)",
+                   "layers": L, "batch": B, "seq_len": S, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+                   "window": w},
+        "target_keys_per_s_kernel_only": round(B * Hkv * S / (tgt_avg * 1e-3), 1),
+        "target_tflops": round(tgt_tflops, 2),
+        "target_frac_bf16_peak": round(tgt_tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "step_tflops": round(step_tflops, 2),
+        "roofline": dominant,
+        "kernels": {"future_target": r_tgt, "attn_fwd": r_fwd},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * kvpop.h -- C ABI of libkvpop.so: the training-time hot path of KVpop
+ * (future-attention target and fixed-budget sparse attention) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources: "KVpop -- Key-Value Cache Compression with Predictive Online
+ * Pruning" (paper text): Section 3 (fixed per-KV-head budget of sinks,
+ * protected window and long-range top-k), Section 3.1 (future-attention
+ * target, Eqs. 2-4), Section 3.2 (transposed-attention target computation,
+ * Eq. 8; running top-k sparse attention), Section 4 (packed training
+ * sequences).  The Korean technical summary of the same paper (gist.science),
+ * Section 2.1, writes the budget as B = s + w + k and Section 2.2 the target
+ * condition d >= t + w.
+ *
+ * Conventions shared by every entry point
+ *  - Layout: contiguous, heads-major.  Q and O are [B, Hq, S, D]; K and V are
+ *    [B, Hkv, S, D]; LSE is [B, Hq, S]; scores are [B, Hkv, S].  A packed
+ *    batch of documents is one sequence (B = 1) with document offsets
+ *    cu_seqlens[0..n_docs] (0 = first, S = last); attention never crosses a
+ *    document boundary.
+ *  - GQA: query head g reads KV head g / (Hq / Hkv).
+ *  - Logit s_{d,t} = softmax_scale * q_d . k_t (softmax_scale <= 0 selects
+ *    1/sqrt(D)).  All logarithms returned are natural logarithms.
+ *  - dtype: KVPOP_BF16 (bfloat16 Q/K/V/O, fp32 accumulation) or KVPOP_F32.
+ *    head_dim must be 64 or 128.
+ *  - Every pointer is device memory owned by the caller, 16-byte aligned,
+ *    except cu_seqlens_host (host memory, read synchronously during the
+ *    call).  The library allocates nothing; workspace is caller-provided and
+ *    sized by kvpop_workspace_size().  The stream is a hipStream_t passed as
+ *    void* (NULL = the default stream); work is enqueued asynchronously.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued; a failed validation returns a non-zero status and leaves the
+ *    outputs untouched.  kvpop_last_error() returns a thread-local message
+ *    for the last failure.  Device faults surface at the caller's next
+ *    synchronisation, as in HIP.  No exception crosses the ABI.
+ *  - No global atomics: results are bitwise reproducible for a fixed shape.
+ */
+#ifndef KVPOP_H
+#define KVPOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvpop_status;
+#define KVPOP_OK 0
+#define KVPOP_EINVAL 1        /* bad argument (null pointer, bad shape, bad offsets) */
+#define KVPOP_EUNSUPPORTED 2  /* unsupported head_dim, dtype or combination */
+#define KVPOP_EWORKSPACE 3    /* workspace smaller than kvpop_workspace_size() */
+#define KVPOP_EHIP 4          /* HIP runtime error, including "no device" */
+
+enum { KVPOP_BF16 = 0, KVPOP_F32 = 1 };
+enum { KVPOP_AGG_SUM = 0, KVPOP_AGG_MAX = 1, KVPOP_AGG_NONE = 2 };
+enum { KVPOP_CALL_FWD_LSE = 0, KVPOP_CALL_FUTURE_TARGET = 1, KVPOP_CALL_BUDGET_MASK_FWD = 2 };
+
+/* cutoff_out sentinels of kvpop_budget_mask_fwd */
+#define KVPOP_CUTOFF_ALL 2147483647 /* fewer than k eligible tokens: all kept */
+#define KVPOP_CUTOFF_NONE (-1)      /* k == 0: no eligible token kept */
+
+typedef struct {
+  int32_t batch;       /* B >= 1 (must be 1 when cu_seqlens is given) */
+  int32_t seqlen;      /* S >= 1 (total packed length with cu_seqlens) */
+  int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t dtype;       /* KVPOP_BF16 or KVPOP_F32: element type of Q, K, V, O */
+  float softmax_scale; /* <= 0: 1/sqrt(D) */
+  const int32_t *cu_seqlens;      /* device [n_docs+1] or NULL (one document per batch row) */
+  const int32_t *cu_seqlens_host; /* the same offsets in host memory (NULL iff cu_seqlens is NULL) */
+  int32_t n_docs;                 /* number of documents when packed, else ignored */
+} kvpop_shape;
+
+/*
+ * Causal attention forward with per-query log-sum-exp.
+ *
+ * For every batch row b, query head g and query d:
+ *   L_d = ln sum_{t <= d, same document} exp(s_{d,t})
+ *   O_d = sum_t exp(s_{d,t} - L_d) v_t
+ * The paper's target is defined through these dense causal probabilities
+ * and its transposed identity is exact with this L (Section 3.2).
+ *
+ *  q [B,Hq,S,D], k, v [B,Hkv,S,D]  inputs (dtype)
+ *  o [B,Hq,S,D]                    output (dtype); may be NULL: LSE only
+ *  lse [B,Hq,S] fp32               output
+ */
+kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const void *k,
+                                const void *v, void *o, float *lse, void *hip_stream);
+
+/*
+ * Future-attention target by one transposed-attention pass (Section 3.2,
+ * Eq. 8): key tiles stay resident, query tiles stream past them, the logits
+ * are recomputed and the given per-query normaliser is subtracted; nothing
+ * of size S x S is stored.  For key t of KV head h and query head g of its
+ * group:
+ *   mass_g(t) = sum_{d >= t + window, same document} exp(s_{d,t} - lse_d)
+ * With mean_over_queries != 0 the mass is divided by N_t, the number of such
+ * queries (the mean of Eq. 2; an empty set gives 0).  Then
+ *   KVPOP_AGG_SUM : target[b,h,t] = ln(sum_g mass_g(t) + eps)
+ *   KVPOP_AGG_MAX : target[b,h,t] = max_g ln(mass_g(t) + eps)   (Eq. 3, max)
+ *   KVPOP_AGG_NONE: target[b,g,t] = ln(mass_g(t) + eps)
+ * An empty set with eps = 0 gives -inf.
+ *
+ *  q [B,Hq,S,D], k [B,Hkv,S,D]      inputs (dtype)
+ *  lse [B,Hq,S] fp32                natural-log normaliser per query: the
+ *                                   dense one from kvpop_attn_fwd_lse makes
+ *                                   the identity exact; the sparse one from
+ *                                   kvpop_budget_mask_fwd is the paper's
+ *                                   approximation.  Precondition:
+ *                                   s_{d,t} - lse_d < 88 (always true for the
+ *                                   dense normaliser, which bounds every
+ *                                   logit of its row).
+ *  window >= 0, eps >= 0
+ *  target [B,Hkv,S] fp32 (SUM, MAX) or [B,Hq,S] fp32 (NONE)  output
+ *  workspace, ws_bytes             >= kvpop_workspace_size(KVPOP_CALL_FUTURE_TARGET, ...)
+ */
+kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const void *k,
+                                 const float *lse, int32_t window, int32_t agg,
+                                 int32_t mean_over_queries, float eps, float *target,
+                                 void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Fixed-budget sparse attention forward (Section 3 budget; Section 3.2
+ * "Running top-k sparse attention").  Per KV head (shared by its query
+ * heads), query d keeps
+ *   - the sinks t < sinks,
+ *   - the protected window d - window < t <= d,
+ *   - among the eligible tokens E_d = [sinks, d - window] (Eq. 4), the topk
+ *     best by static priority: rank(t) orders scores descending, ties (and
+ *     -0.0 vs +0.0) to the lower index, NaN as -inf; with
+ *     c_d = the topk-th smallest rank in E_d, token t in E_d is kept iff
+ *     rank(t) <= c_d.
+ * It returns the attention output and natural-log LSE under that mask (the
+ * sparse normaliser the paper reuses for its target).  A row with nothing
+ * kept (sinks = window = topk = 0) gets lse = -inf and O = 0.
+ *
+ *  q, k, v                          inputs as for kvpop_attn_fwd_lse (cu_seqlens must be NULL)
+ *  scores [B,Hkv,S] fp32            static priorities
+ *  sinks, window, topk >= 0
+ *  o [B,Hq,S,D] (dtype), lse [B,Hq,S] fp32   outputs
+ *  rank_out [B,Hkv,S] int32         optional (NULL): rank(t), a permutation of 0..S-1
+ *  cutoff_out [B,Hkv,S] int32       optional (NULL): c_d, or KVPOP_CUTOFF_ALL
+ *                                   when |E_d| < topk, or KVPOP_CUTOFF_NONE
+ *                                   when topk == 0
+ *  workspace, ws_bytes              >= kvpop_workspace_size(KVPOP_CALL_BUDGET_MASK_FWD, ...)
+ */
+kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, const void *k,
+                                   const void *v, const float *scores, int32_t sinks,
+                                   int32_t window, int32_t topk, void *o, float *lse,
+                                   int32_t *rank_out, int32_t *cutoff_out, void *workspace,
+                                   size_t ws_bytes, void *hip_stream);
+
+/*
+ * Bytes of workspace the call `which` (KVPOP_CALL_*) needs for this shape
+ * and these budget parameters (sinks, window and topk matter only for
+ * KVPOP_CALL_BUDGET_MASK_FWD; pass 0 otherwise).  Returns 0 for an invalid
+ * shape and for calls that need none (KVPOP_CALL_FWD_LSE).
+ */
+size_t kvpop_workspace_size(int32_t which, const kvpop_shape *shape, int32_t sinks,
+                            int32_t window, int32_t topk);
+
+/* Static description of a status code. */
+const char *kvpop_status_str(kvpop_status status);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char *kvpop_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOP_H */

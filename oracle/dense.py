@@ -83,7 +83,7 @@ def _row_lse(logits: np.ndarray, allowed: np.ndarray) -> np.ndarray:
 
 def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = None,
                    lse_in: Optional[np.ndarray] = None, need_output: bool = True,
-                   heads: Optional[list] = None, row_block: int = 256):
+                   heads: Optional[list] = None, row_block: int = 256, need_abs_output: bool = False):
     """One pass over the dense causal attention matrix, row block by row block.
 
     For every (b, g) and query row d it computes the logits s_{d,t} =
@@ -102,8 +102,12 @@ def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = No
     approximation, [P] Section 3.2); O and the returned LSE are still the
     dense ones.
 
-    Returns dict(lse [B,Hq,S], out [B,Hq,S,D] or None, colmass [B,Hq,S] or None).
-    `heads` restricts the pass to a list of (b, g) pairs (others stay NaN).
+    With `need_abs_output`, also abs_out = sum_t a^g_{d,t} |v^h_t| (used only
+    to bound the rounding error of a reduced-precision output).
+
+    Returns dict(lse [B,Hq,S], out [B,Hq,S,D] or None, colmass [B,Hq,S] or
+    None, abs_out or None).  `heads` restricts the pass to a list of (b, g)
+    pairs (others stay NaN).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -119,12 +123,13 @@ def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = No
     lse = np.full((B, Hq, S), np.nan)
     out = np.full((B, Hq, S, D), np.nan) if (need_output and v is not None) else None
     colmass = np.full((B, Hq, S), np.nan) if window is not None else None
+    abs_out = np.full((B, Hq, S, D), np.nan) if (need_abs_output and v is not None) else None
     if heads is None:
         heads = [(b, g) for b in range(B) for g in range(Hq)]
     for (b, g) in heads:
         h = g // G
         kh = k[b, h]
-        vh = None if out is None else np.asarray(v[b, h], dtype=np.float64)
+        vh = None if v is None else np.asarray(v[b, h], dtype=np.float64)
         if colmass is not None:
             colmass[b, g] = 0.0
         for r0 in range(0, S, row_block):
@@ -132,11 +137,13 @@ def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = No
             logits, allowed, c0 = _causal_logits(q[b, g, rows], kh, rows, start, sc)
             L = _row_lse(logits, allowed)
             lse[b, g, rows] = L
-            if out is not None or colmass is not None:
+            if out is not None or colmass is not None or abs_out is not None:
                 with np.errstate(under="ignore", invalid="ignore"):
                     A = np.where(allowed, np.exp(logits - L[:, None]), 0.0)
             if out is not None:
                 out[b, g, rows] = A @ vh[c0:rows[-1] + 1]
+            if abs_out is not None:
+                abs_out[b, g, rows] = A @ np.abs(vh[c0:rows[-1] + 1])
             if colmass is not None:
                 cols = np.arange(c0, rows[-1] + 1)
                 fut = allowed & (cols[None, :] <= rows[:, None] - window)
@@ -147,7 +154,7 @@ def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = No
                 else:
                     Af = np.where(fut, A, 0.0)
                 colmass[b, g, c0:rows[-1] + 1] += Af.sum(axis=0)
-    return {"lse": lse, "out": out, "colmass": colmass}
+    return {"lse": lse, "out": out, "colmass": colmass, "abs_out": abs_out}
 
 
 def future_count(S: int, cu, window: int) -> np.ndarray:

@@ -1,0 +1,206 @@
+"""GPU parity of the dense forward (LSE, output) and the transposed target pass
+against the fp64 CPU oracle, on seeded synthetic inputs.  Runs on an MI355X."""
+import math
+import sys
+
+import pytest
+import torch
+
+import synth
+from oracle import dense
+from tests.parity import assert_lse_close, assert_out_bounded, assert_target_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(t):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) and k in ("q", "k", "v", "scores") else v)
+            for k, v in t.items()}
+
+
+def oracle_ref(q, k, v, cu, w, heads=None, need_output=True, agg=dense.AGG_SUM, mean=False, eps=0.0):
+    q64, k64 = dense.to_f64(q), dense.to_f64(k)
+    v64 = None if v is None else dense.to_f64(v)
+    r = dense.attention_pass(q64, k64, v64, cu=cu, window=w, need_output=need_output, heads=heads,
+                             need_abs_output=need_output and v is not None)
+    return r
+
+
+def run_gpu(kv, q, k, v, cu, w, agg="sum", mean=False, eps=0.0, need_output=True):
+    o, lse = kv.attn_fwd_lse(q, k, v, cu_seqlens=cu, need_output=need_output)
+    tgt = kv.future_target(q, k, lse, w, agg=agg, mean_over_queries=mean, eps=eps, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return o, lse, tgt
+
+
+U = {"torch.bfloat16": 2.0 ** -8, "torch.float32": 2.0 ** -16}  # unit roundoff used for P and O
+AGG = {"sum": dense.AGG_SUM, "max": dense.AGG_MAX, "none": dense.AGG_NONE}
+
+
+def test_tiny_config_all_modes(kvpop_lib):
+    """S=512, D=64, fp32, K scaled by 1.5, w=16, seed 0."""
+    t = synth.make_workload("tiny", device=DEV)
+    q, k, v, w = t["q"], t["k"], t["v"], t["window"]
+    say("tiny: fwd + target")
+    r = oracle_ref(q, k, v, None, w)
+    o, lse, _ = run_gpu(kvpop_lib, q, k, v, None, w)
+    e1 = assert_lse_close(lse, r["lse"])
+    e2 = assert_out_bounded(o, r["out"], r["abs_out"], u=U[str(q.dtype)])
+    for agg, mean, eps in [("sum", False, 0.0), ("none", False, 0.0), ("max", True, 1e-6), ("sum", True, 1e-6),
+                           ("none", True, 0.0)]:
+        tg = kvpop_lib.future_target(q, k, lse, w, agg=agg, mean_over_queries=mean, eps=eps)
+        ref = dense.target_from_colmass(r["colmass"], 1, None, w, AGG[agg], mean, eps)
+        e3 = assert_target_close(tg, ref, what=f"target[{agg},{mean},{eps}]")
+        say(f"  {agg} mean={mean} eps={eps}: lse err {e1:.2e} out rel {e2:.2e} target err {e3:.2e}")
+
+
+CASES = [
+    # S, Hq, Hkv, D, dtype, docs, w
+    (1, 1, 1, 64, "bf16", 1, 0),
+    (37, 2, 1, 64, "bf16", 1, 3),
+    (100, 4, 1, 128, "bf16", 1, 0),
+    (257, 4, 2, 128, "bf16", 3, 5),
+    (300, 8, 1, 128, "bf16", 1, 64),
+    (600, 4, 4, 64, "bf16", 4, 17),
+    (520, 2, 2, 128, "bf16", 2, 600),
+    (700, 6, 3, 128, "bf16", 5, 1),
+    (333, 4, 1, 64, "f32", 2, 9),
+    (1100, 4, 1, 128, "bf16", 2, 128),
+]
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,dt,docs,w", CASES)
+def test_random_shapes(kvpop_lib, S, Hq, Hkv, D, dt, docs, w):
+    seed = S * 7 + Hq + D + docs
+    say(f"random shape S={S} Hq={Hq} Hkv={Hkv} D={D} {dt} docs={docs} w={w}")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, dt, seed, device=DEV, heavy_hitters=S >= 200)
+    cu = None
+    if docs > 1:
+        cu = synth.cu_seqlens_from_lengths(synth.doc_lengths(S, docs, 0, seed) if S > docs else [S])
+    q, k, v = t["q"], t["k"], t["v"]
+    r = oracle_ref(q, k, v, cu.tolist() if cu is not None else None, w)
+    o, lse, tg = run_gpu(kvpop_lib, q, k, v, cu, w)
+    assert_lse_close(lse, r["lse"])
+    assert_out_bounded(o, r["out"], r["abs_out"], u=U[str(q.dtype)])
+    ref = dense.target_from_colmass(r["colmass"], Hkv, cu.tolist() if cu is not None else None, w, dense.AGG_SUM)
+    assert_target_close(tg, ref)
+    tn = kvpop_lib.future_target(q, k, lse, w, agg="none", cu_seqlens=cu)
+    refn = dense.target_from_colmass(r["colmass"], Hkv, cu.tolist() if cu is not None else None, w, dense.AGG_NONE)
+    assert_target_close(tn, refn, what="target none")
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,w", [(513, 4, 1, 16), (2048, 8, 2, 64)])
+def test_target_fed_with_oracle_lse(kvpop_lib, S, Hq, Hkv, w):
+    """The target kernel alone: it receives the oracle's own LSE (fp32)."""
+    say(f"target with oracle lse S={S}")
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 99 + S, device=DEV, heavy_hitters=True)
+    q, k = t["q"], t["k"]
+    r = oracle_ref(q, k, None, None, w, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    tg = kvpop_lib.future_target(q, k, lse, w, agg="max", mean_over_queries=True, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = dense.target_from_colmass(r["colmass"], Hkv, None, w, dense.AGG_MAX, True, 1e-6)
+    assert_target_close(tg, ref)
+
+
+def test_qwen4k_full(kvpop_lib):
+    """S=4096, 32q/8kv, D=128, bf16, 1% heavy hitters, w=64: every head."""
+    t = to_dev(synth.make_workload("qwen4k", device=DEV))
+    q, k, v, w = t["q"], t["k"], t["v"], t["window"]
+    say("qwen4k: gpu")
+    o, lse, tg = run_gpu(kvpop_lib, q, k, v, None, w)
+    say("qwen4k: oracle")
+    r = oracle_ref(q, k, v, None, w)
+    e1 = assert_lse_close(lse, r["lse"])
+    e2 = assert_out_bounded(o, r["out"], r["abs_out"], u=U[str(q.dtype)])
+    e3 = assert_target_close(tg, dense.target_from_colmass(r["colmass"], 8, None, w, dense.AGG_SUM))
+    say(f"qwen4k: lse {e1:.2e} out {e2:.2e} target {e3:.2e}")
+
+
+def test_packed16k_sampled_heads(kvpop_lib):
+    """S=16384 packed as 6 documents, w=128: KV heads 0 and 5 (8 query heads)."""
+    t = synth.make_workload("packed16k", device=DEV)
+    q, k, v, w, cu = t["q"], t["k"], t["v"], t["window"], t["cu_seqlens"]
+    say("packed16k docs", synth.doc_lengths_of(cu, 16384))
+    o, lse, tg = run_gpu(kvpop_lib, q, k, v, cu, w)
+    heads = [(0, g) for g in list(range(0, 4)) + list(range(20, 24))]
+    r = oracle_ref(q, k, v, cu.tolist(), w, heads=heads)
+    gsel = [g for _, g in heads]
+    assert_lse_close(lse[:, gsel], r["lse"][:, gsel])
+    assert_out_bounded(o[:, gsel], r["out"][:, gsel], r["abs_out"][:, gsel])
+    ref = dense.target_from_colmass(r["colmass"], 8, cu.tolist(), w, dense.AGG_SUM)
+    assert_target_close(tg[:, [0, 5]], ref[:, [0, 5]])
+
+
+@pytest.mark.parametrize("layer,b,h", [(0, 1, 3), (35, 0, 6)])
+def test_stack36_sampled(kvpop_lib, layer, b, h):
+    """Full Qwen3-4B-shaped layer (B=2, S=16384, 32q/8kv/128, w=128) in the
+    launch configuration the bench times; one (batch row, KV head) group is
+    checked against the oracle."""
+    t = synth.make_workload("stack36", layer=layer, device=DEV)
+    q, k, v, w = t["q"], t["k"], t["v"], t["window"]
+    say(f"stack36 layer {layer}: gpu")
+    o, lse, tg = run_gpu(kvpop_lib, q, k, v, None, w)
+    heads = [(b, g) for g in range(4 * h, 4 * h + 4)]
+    say(f"stack36 layer {layer}: oracle on {heads}")
+    r = oracle_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], None, w, heads=[(0, g) for _, g in heads])
+    gs = [g for _, g in heads]
+    assert_lse_close(lse[b:b + 1, gs], r["lse"][:, gs])
+    assert_out_bounded(o[b:b + 1, gs], r["out"][:, gs], r["abs_out"][:, gs])
+    ref = dense.target_from_colmass(r["colmass"], 8, None, w, dense.AGG_SUM)
+    assert_target_close(tg[b:b + 1, h:h + 1], ref[:, h:h + 1])
+
+
+def test_window_beyond_documents_gives_minus_inf(kvpop_lib):
+    t = synth.make_qkv(1, 300, 4, 2, 128, "bf16", 5, device=DEV)
+    cu = torch.tensor([0, 50, 120, 300], dtype=torch.int32)
+    _, lse = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], cu_seqlens=cu, need_output=False)
+    tg = kvpop_lib.future_target(t["q"], t["k"], lse, 180, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(tg))
+
+
+def test_lse_only_matches_full_forward(kvpop_lib):
+    t = synth.make_qkv(2, 777, 8, 2, 128, "bf16", 8, device=DEV)
+    _, l1 = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], need_output=False)
+    _, l2 = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], need_output=True)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2)
+
+
+def test_bitwise_determinism(kvpop_lib):
+    t = synth.make_qkv(1, 3000, 8, 2, 128, "bf16", 11, device=DEV, heavy_hitters=True)
+    o1, l1, t1 = run_gpu(kvpop_lib, t["q"], t["k"], t["v"], None, 64)
+    o2, l2, t2 = run_gpu(kvpop_lib, t["q"], t["k"], t["v"], None, 64)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(t1, t2)
+    torch.testing.assert_close(t1.isneginf(), t2.isneginf())
+
+
+def test_invariant_total_mass_at_zero_window(kvpop_lib):
+    """Row sums are 1, so with w = 0 the masses of a KV head's group add up
+    to G * (number of queries), whatever the inputs."""
+    S, Hq, Hkv = 2500, 8, 2
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 21, device=DEV, heavy_hitters=True)
+    _, lse = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], need_output=False)
+    tg = kvpop_lib.future_target(t["q"], t["k"], lse, 0)
+    torch.cuda.synchronize()
+    tot = torch.exp(tg.double()).sum(dim=-1)
+    assert torch.allclose(tot, torch.full_like(tot, (Hq // Hkv) * S), rtol=1e-3)
+    assert math.isfinite(float(tot.sum()))
+
+
+def test_invariant_mass_holds_at_full_size(kvpop_lib):
+    """At the full layer size (B=2, S=16384) the w=0 total-mass invariant
+    checks every key of every head."""
+    t = synth.make_workload("stack36", layer=7, device=DEV)
+    _, lse = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], need_output=False)
+    tg = kvpop_lib.future_target(t["q"], t["k"], lse, 0)
+    torch.cuda.synchronize()
+    tot = torch.exp(tg.double()).sum(dim=-1)
+    assert torch.allclose(tot, torch.full_like(tot, 4 * 16384), rtol=1e-3)
