@@ -35,6 +35,9 @@ def hipcc() -> str:
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: the exp/sum epilogues read
+            # them directly instead of copying out of AGPRs first
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-result"]
 
 

@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   __shared__ int kpos_lds[KT];
   __shared__ int krank_lds[KT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
   const int HG = p.HG, QB = 32 * (4 / HG), NG = p.G / HG;
   const int nqb = (p.S + QB - 1) / QB;

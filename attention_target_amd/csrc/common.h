@@ -47,6 +47,29 @@ __device__ __forceinline__ void mma(f32x16 &acc, const Frag<float> &a, const Fra
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
 }
+// d = a * b + c with a separate addend tile (c is not overwritten).
+__device__ __forceinline__ f32x16 mma_add(const Frag<bf16> &a, const Frag<bf16> &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_add(const Frag<float> &a, const Frag<float> &b, const f32x16 &c) {
+  f32x16 d = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+#pragma unroll
+  for (int e = 1; e < 4; ++e) d = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[e], b.lo[e], d, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], d, 0, 0, 0);
+  return d;
+}
+
+// Multiplies a fragment by x, rounding each element back to the fragment type
+// (round to nearest even for bf16).
+__device__ __forceinline__ void scale_frag(Frag<bf16> &f, float x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)((float)f.v[e] * x);
+}
+__device__ __forceinline__ void scale_frag(Frag<float> &f, float x) {
+  f.lo *= x;
+  f.hi *= x;
+}
 
 // Eight consecutive elements starting at p (16-byte aligned).
 __device__ __forceinline__ void load_frag(Frag<bf16> &f, const bf16 *p) {

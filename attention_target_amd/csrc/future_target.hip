@@ -13,13 +13,16 @@
 //    registers (the MFMA A operand) for the whole block.
 //  * Query tiles of 32 positions stream through double-buffered, swizzled
 //    LDS together with -L_d*log2(e); for every query head of the group each
-//    wave computes S^T (64 keys x 32 queries) with MFMA and, per element,
-//    p = exp2(s * scale*log2e - L*log2e) added into per-lane fp32 sums.  No
-//    running max is needed: with the dense normaliser s_{d,t} <= L_d.
+//    wave computes S = Q K'^T (32 queries x 64 keys) with MFMA.  K' is K
+//    multiplied by scale*log2(e) (rounded to the input type once per block)
+//    and the MFMA addend is -L_d*log2(e), so the accumulator is directly the
+//    exp2 argument: per element only exp2 and one add into the per-lane sum
+//    of the lane's key remain on the VALU.  No running max is needed: with
+//    the dense normaliser s_{d,t} <= L_d.
 //  * The masks d >= t + w and "inside the document" are applied only on the
 //    sub-tiles that cross them.
-//  * At the end each wave reduce-scatters its 32 per-lane sums (31 shuffles)
-//    and writes one partial per key and query chunk into the workspace; a
+//  * At the end the two halves of each wave add their sums (one shuffle)
+//    and write one partial per key and query chunk into the workspace; a
 //    second small kernel adds the chunks in a fixed order, applies the mean,
 //    epsilon and the aggregation over query heads, and takes the log.  There
 //    are no atomics, so results are bitwise reproducible.
@@ -69,7 +72,7 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
   __shared__ __align__(16) char q_lds[2][QBYTES];
-  __shared__ float nl_lds[2][32];
+  __shared__ __align__(16) float nl_lds[2][32];
 
   // ---- which block ----
   const int per_xcd = (p.total_blocks + 7) / 8;
@@ -104,20 +107,27 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
   if (j < 0) return;
   const int t0 = r * TGT_KT;  // doc-local first key of the block
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
   const int tw = t0 + 64 * wave;  // doc-local first key of this wave
   const int w = p.window;
 
-  // ---- resident K fragments (A operand) ----
+  // ---- resident K fragments (B operand), pre-multiplied by scale*log2(e) ----
+  // S = Q K'^T puts queries on the rows (registers) and keys on the columns
+  // (lanes), so every lane accumulates the column sum of one key.  With K'
+  // holding scale*log2(e) and the MFMA addend holding -L_d*log2(e), the
+  // accumulator is already the exp2 argument s_{d,t}*log2(e) - L_d*log2(e).
   const T *kbase = reinterpret_cast<const T *>(p.k) + ((size_t)b * p.Hkv + h) * (size_t)p.S * D;
   Frag<T> kf[2][NJ];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int key = min(tw + 32 * rb + col, n - 1);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int key = min(tw + 32 * cb + col, n - 1);
     const T *kr = kbase + (size_t)(dstart + key) * D + 8 * hf;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) load_frag(kf[rb][jj], kr + 16 * jj);
+    for (int jj = 0; jj < NJ; ++jj) {
+      load_frag(kf[cb][jj], kr + 16 * jj);
+      scale_frag(kf[cb][jj], p.scale_log2);
+    }
   }
 
   // ---- query sub-tiles of this chunk ----
@@ -127,7 +137,7 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
   const int n_sub = (cq1 - qs_al + 31) / 32;
   const int n_it = p.G * n_sub;
 
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   u32x4 qreg[Q_PER_THREAD];
   float nlreg = 0.f;
 
@@ -149,7 +159,7 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
     }
     if (tid < 32) {
       const int qrow = dstart + min(q0 + tid, n - 1);
-      nlreg = -p.lse[((size_t)b * p.Hq + g) * p.S + qrow] * kLog2e;
+      nlreg = p.lse[((size_t)b * p.Hq + g) * p.S + qrow];
     }
   };
   auto store = [&](int buf) {
@@ -159,36 +169,20 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
       const int rr = li / CPR, ch = li % CPR;
       *reinterpret_cast<u32x4 *>(q_lds[buf] + QTile::off(rr, ch)) = qreg[c];
     }
-    if (tid < 32) nl_lds[buf][tid] = nlreg;
+    if (tid < 32) nl_lds[buf][tid] = -nlreg * kLog2e;
   };
   auto write_partial = [&](int hp) {
-    // reduce-scatter the 32 per-lane sums across the 32 lanes of each half
-    float vals[32];
+    // the two lane halves hold complementary query rows of the same key
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      vals[i] = acc[0][i];
-      vals[16 + i] = acc[1][i];
+    for (int cb = 0; cb < 2; ++cb) {
+      float tot = acc[cb][0] + acc[cb][1];
+      tot += __shfl_xor(tot, 32);
+      const int key = tw + 32 * cb + col;
+      if (hf == 0 && key < n) p.part[(((size_t)b * p.Hp + hp) * p.nch_max + j) * p.S + dstart + key] = tot;
+      acc[cb][0] = acc[cb][1] = 0.f;
     }
-#pragma unroll
-    for (int st = 0; st < 5; ++st) {
-      const int m = 16 >> st;
-      const bool upper = (lane & m) != 0;
-#pragma unroll
-      for (int i = 0; i < m; ++i) {
-        const float send = upper ? vals[i] : vals[i + m];
-        const float keep = upper ? vals[i + m] : vals[i];
-        vals[i] = keep + __shfl_xor(send, m);
-      }
-    }
-    const int rsel = lane & 31;
-    const int kk = 32 * (rsel / 16) + c_row(rsel % 16, hf);
-    const int key = tw + kk;
-    if (key < n) p.part[(((size_t)b * p.Hp + hp) * p.nch_max + j) * p.S + dstart + key] = vals[0];
-    acc[0] = f32x16{};
-    acc[1] = f32x16{};
   };
 
-  const float c = p.scale_log2;
   prefetch(0);
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
@@ -200,31 +194,45 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
     q_of(it, gg, q0);
     const bool any = (q0 + 31 >= tw + w) && (tw < n);
     if (any) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      // addend: -L*log2(e) of the query row held by each register
+      f32x16 cadd;
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        Frag<T> bq;
-        QTile::read(bq, q_lds[buf], col, 16 * jj + 8 * hf);
-        mma(s[0], kf[0][jj], bq);
-        mma(s[1], kf[1][jj], bq);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl_lds[buf][8 * i4 + 4 * hf]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cadd[4 * i4 + e] = v4[e];
       }
-      const float nl = nl_lds[buf][col];
+      f32x16 s[2];
+      {
+        Frag<T> a;
+        QTile::read(a, q_lds[buf], col, 8 * hf);
+        s[0] = mma_add(a, kf[0][0], cadd);
+        s[1] = mma_add(a, kf[1][0], cadd);
+      }
+#pragma unroll
+      for (int jj = 1; jj < NJ; ++jj) {
+        Frag<T> a;
+        QTile::read(a, q_lds[buf], col, 16 * jj + 8 * hf);
+        mma(s[0], a, kf[0][jj]);
+        mma(s[1], a, kf[1][jj]);
+      }
       const bool interior = (q0 >= tw + 63 + w) && (q0 + 31 < n) && (tw + 63 < n);
       if (interior) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[rb][i] += fast_exp2(__builtin_fmaf(s[rb][i], c, nl));
+          for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i]);
       } else {
-        const int d = q0 + col;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int cb = 0; cb < 2; ++cb) {
+          const int t = tw + 32 * cb + col;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int t = tw + 32 * rb + c_row(i, hf);
-            const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, nl));
-            acc[rb][i] += (d >= t + w && d < n && t < n) ? pv : 0.f;
+            const int d = q0 + c_row(i, hf);
+            const float pv = fast_exp2(s[cb][i]);
+            acc[cb][i & 1] += (d >= t + w && d < n && t < n) ? pv : 0.f;
           }
+        }
       }
     }
     if constexpr (!SUM_HEADS) {
