@@ -13,7 +13,11 @@
 // wave owns 32 queries of one head and computes S^T = K Q^T with MFMA: a lane
 // then owns one query column, so the online-softmax max and sum are reductions
 // over the lane's registers plus one exchange with the other lane half.  P^T
-// (bf16) is directly the B operand of O^T = V^T P^T; V is transposed into LDS.
+// (bf16) is directly the B operand of O^T = V^T P^T.  V stays in its natural
+// row layout in LDS and the V^T operand is gathered with gfx950's transposed
+// LDS reads.  K/V tiles are double-buffered (one barrier per tile), the
+// softmax scale is folded into the exp2 argument, and the running output is
+// rescaled only when a row maximum grows by more than a fixed margin.
 #pragma once
 
 #include "common.h"
@@ -38,15 +42,51 @@ struct FwdParams {
 
 template <typename T, int D>
 struct FwdTiles {
-  static constexpr int KT = 64;      // keys per tile
-  static constexpr int VT_LD = 68;   // V^T row length (64 keys + pad), elements
-  static constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
-  static constexpr int K_CHUNKS = KT * D / EPC;           // 16-byte chunks of a K tile
-  static constexpr int K_PER_THREAD = K_CHUNKS / 256;
-  static constexpr int V_ITEMS = (KT / 4) * (D / EPC);    // (4-key group, chunk) items
-  static constexpr int V_PER_THREAD = (V_ITEMS + 255) / 256;
-  static_assert(K_CHUNKS % 256 == 0, "K tile must split evenly over 256 threads");
+  static constexpr int KT = 64;                           // keys per tile
+  static constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                     // 16-byte chunks per row
+  static constexpr int K_BYTES = KT * D * (int)sizeof(T);
+  // V rows keep their natural layout, padded by 32 bytes so that the
+  // transposed 8-byte reads of four consecutive rows hit distinct banks.
+  static constexpr int V_LD = D * (int)sizeof(T) + 32;
+  static constexpr int V_BYTES = KT * V_LD;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int PER_THREAD = KT * CPR / 256;       // chunks of K (and of V) per thread
+  static_assert(KT * CPR % 256 == 0, "tile must split evenly over 256 threads");
 };
+
+// Rescaling of the running output is skipped until a row maximum grows by
+// more than this many powers of two; probabilities then stay below 2^TAU.
+constexpr float kLazyRescaleLog2 = 8.f;
+
+// A operand of O^T = V^T P^T for the 16-key step j and the 32 head-dim rows
+// of block nb: lane l needs V[keys 16j + 4*hf + {0..3} and 16j + 8 + 4*hf +
+// {0..3}][32*nb + l%32] (the key order of the P^T fragment).
+__device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int v_ld, int j, int nb, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  // ds_read_tr16_b64: within each group of 16 lanes, lane i returns element
+  // i%4 of the 4-element chunks read by lanes i/4, i/4+4, i/4+8 and i/4+12.
+  // Lane jj of a group therefore reads row k0 + jj/4, columns d0 + 4*(jj%4).
+  const int hf = lane >> 5, grp = (lane >> 4) & 1, jj = lane & 15;
+  const int row = 16 * j + 4 * hf + (jj >> 2);
+  const int colb = 2 * (32 * nb + 16 * grp + 4 * (jj & 3));
+  const char *p0 = vl + row * v_ld + colb;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)(p0 + 8 * v_ld));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  a.v = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int v_ld, int j, int nb, int lane) {
+  const int hf = lane >> 5, d = 32 * nb + (lane & 31);
+  const float *c0 = reinterpret_cast<const float *>(vl + (16 * j + 4 * hf) * v_ld) + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a.lo[e] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(c0) + e * v_ld);
+    a.hi[e] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(c0) + (8 + e) * v_ld);
+  }
+}
 
 template <typename T, int D, bool WITH_O, bool SPARSE>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
@@ -55,14 +95,15 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   constexpr int NJ = D / 16;  // k-steps over the head dimension
   constexpr int NB = D / 32;  // 32-dim blocks of O^T
   constexpr int KT = Tiles::KT;
-  constexpr int VT_LD = Tiles::VT_LD;
   constexpr int EPC = Tiles::EPC;
-  constexpr int CPR = D / EPC;  // chunks per row
+  constexpr int CPR = Tiles::CPR;
+  constexpr int PT = Tiles::PER_THREAD;
+  constexpr int V_LD = Tiles::V_LD;
 
-  __shared__ __align__(16) char k_lds[KT * D * sizeof(T)];
-  __shared__ __align__(16) T vt_lds[D * VT_LD];
-  __shared__ int kpos_lds[KT];
-  __shared__ int krank_lds[KT];
+  // two stages of (K tile, V tile): one barrier per tile
+  __shared__ __align__(16) char smem[2][Tiles::STAGE];
+  __shared__ int kpos_lds[2][KT];
+  __shared__ int krank_lds[2][KT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
@@ -116,12 +157,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   f32x16 o_acc[WITH_O ? NB : 1];
 #pragma unroll
   for (int nb = 0; nb < (WITH_O ? NB : 1); ++nb) o_acc[nb] = f32x16{};
+  // Running maximum (in log2 units, i.e. already times scale*log2e) and the
+  // running sum of this lane half's keys; the halves are added at the end.
   float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.scale_log2;
 
-  // Prefetch registers for one K/V tile.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 kreg[Tiles::K_PER_THREAD];
-  u32x4 vreg[Tiles::V_PER_THREAD][4];
+  u32x4 kreg[PT], vreg[PT];
   int my_kpos = INT32_MAX, my_krank = 0;
 
   auto key_of = [&](int tile, int r, bool &valid) -> int {
@@ -140,25 +182,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
 
   auto prefetch = [&](int tile) {
 #pragma unroll
-    for (int c = 0; c < Tiles::K_PER_THREAD; ++c) {
-      const int li = tid + 256 * c;
+    for (int cc = 0; cc < PT; ++cc) {
+      const int li = tid + 256 * cc;
       const int r = li / CPR, ch = li % CPR;
       bool valid;
       const int t = key_of(tile, r, valid);
-      kreg[c] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)t * D + ch * EPC);
-    }
-#pragma unroll
-    for (int it = 0; it < Tiles::V_PER_THREAD; ++it) {
-      const int item = tid + 256 * it;
-      if (item < Tiles::V_ITEMS) {
-        const int kg = item / CPR, ch = item % CPR;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bool valid;
-          const int t = key_of(tile, 4 * kg + e, valid);
-          vreg[it][e] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)t * D + ch * EPC);
-        }
-      }
+      kreg[cc] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)t * D + ch * EPC);
+      vreg[cc] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)t * D + ch * EPC);
     }
     if (tid < KT) {
       bool valid;
@@ -168,45 +198,26 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < Tiles::K_PER_THREAD; ++c) {
-      const int li = tid + 256 * c;
+    for (int cc = 0; cc < PT; ++cc) {
+      const int li = tid + 256 * cc;
       const int r = li / CPR, ch = li % CPR;
-      *reinterpret_cast<u32x4 *>(k_lds + KTile::off(r, ch)) = kreg[c];
-    }
-#pragma unroll
-    for (int it = 0; it < Tiles::V_PER_THREAD; ++it) {
-      const int item = tid + 256 * it;
-      if (item < Tiles::V_ITEMS) {
-        const int kg = item / CPR, ch = item % CPR;
-        const T *e0 = reinterpret_cast<const T *>(&vreg[it][0]);
-        const T *e1 = reinterpret_cast<const T *>(&vreg[it][1]);
-        const T *e2 = reinterpret_cast<const T *>(&vreg[it][2]);
-        const T *e3 = reinterpret_cast<const T *>(&vreg[it][3]);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          T *dst = vt_lds + (ch * EPC + e) * VT_LD + 4 * kg;
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 w = {e0[e], e1[e], e2[e], e3[e]};
-            *reinterpret_cast<bf16x4 *>(dst) = w;
-          } else {
-            f32x4 w = {e0[e], e1[e], e2[e], e3[e]};
-            *reinterpret_cast<f32x4 *>(dst) = w;
-          }
-        }
-      }
+      *reinterpret_cast<u32x4 *>(smem[buf] + KTile::off(r, ch)) = kreg[cc];
+      *reinterpret_cast<u32x4 *>(smem[buf] + Tiles::K_BYTES + r * V_LD + 16 * ch) = vreg[cc];
     }
     if (tid < KT) {
-      kpos_lds[tid] = my_kpos;
-      krank_lds[tid] = my_krank;
+      kpos_lds[buf][tid] = my_kpos;
+      krank_lds[buf][tid] = my_krank;
     }
   };
 
-  if (n_tiles > 0) prefetch(0);
+  if (n_tiles > 0) {
+    prefetch(0);
+    store_tile(0);
+  }
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();
-    store_tile();
+    const int buf = tile & 1;
     __syncthreads();
     if (tile + 1 < n_tiles) prefetch(tile + 1);
 
@@ -217,100 +228,101 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
       any = any && tb <= wq_last && tb + KT - 1 >= wds_first;
       full = tb >= wds_last && tb + KT - 1 <= q0 && tb + KT - 1 < kend;
     }
-    if (!any) continue;
-
-    f32x16 s[2];
+    if (any) {
+      const char *kl = smem[buf];
+      const char *vl = smem[buf] + Tiles::K_BYTES;
+      f32x16 s[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      s[rb] = f32x16{};
+      for (int rb = 0; rb < 2; ++rb) {
+        s[rb] = f32x16{};
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        Frag<T> a;
-        KTile::read(a, k_lds, 32 * rb + col, 16 * j + 8 * hf);
-        mma(s[rb], a, qf[j]);
-      }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[rb][i] * p.scale_log2;
-        if (!full) {
-          const int r = 32 * rb + c_row(i, hf);
-          bool ok;
-          if constexpr (!SPARSE) {
-            const int t = tb + r;
-            ok = qvalid && t <= qpos && t >= qdoc_start;
-          } else {
-            const int t = kpos_lds[r];
-            const int rk = krank_lds[r];
-            ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
-          }
-          x = ok ? x : -INFINITY;
-        }
-        s[rb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float sum = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(s[rb][i] - m_use);
-        s[rb][i] = pv;
-        sum += pv;
-      }
-    }
-    sum += __shfl_xor(sum, 32);
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
-
-    if constexpr (WITH_O) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o_acc[nb] *= alpha;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Frag<T> pf;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf.v[e] = (bf16)s[j >> 1][8 * (j & 1) + e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pf.lo[e] = s[j >> 1][8 * (j & 1) + e];
-            pf.hi[e] = s[j >> 1][8 * (j & 1) + 4 + e];
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const T *vr = vt_lds + (32 * nb + col) * VT_LD + 16 * j + 4 * hf;
+        for (int j = 0; j < NJ; ++j) {
           Frag<T> a;
-          if constexpr (sizeof(T) == 2) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vr);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vr + 8);
-            a.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          } else {
-            a.lo = *reinterpret_cast<const f32x4 *>(vr);
-            a.hi = *reinterpret_cast<const f32x4 *>(vr + 8);
+          KTile::read(a, kl, 32 * rb + col, 16 * j + 8 * hf);
+          mma(s[rb], a, qf[j]);
+        }
+      }
+
+      // masked row maximum of the raw logits
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = s[rb][i];
+          if (!full) {
+            const int r = 32 * rb + c_row(i, hf);
+            bool ok;
+            if constexpr (!SPARSE) {
+              const int t = tb + r;
+              ok = qvalid && t <= qpos && t >= qdoc_start;
+            } else {
+              const int t = kpos_lds[buf][r];
+              const int rk = krank_lds[buf][r];
+              ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+            }
+            x = ok ? x : -INFINITY;
           }
-          mma(o_acc[nb], a, pf);
+          s[rb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxc = mx * c;
+      // lazy rescale: only when some row's maximum grew by more than 2^TAU
+      if (__ballot(mxc > m_run + kLazyRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, mxc);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        if constexpr (WITH_O) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o_acc[nb] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, -m_use));
+          s[rb][i] = pv;
+          l_run += pv;
+        }
+      }
+
+      if constexpr (WITH_O) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frag<T> pf;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf.v[e] = (bf16)s[j >> 1][8 * (j & 1) + e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pf.lo[e] = s[j >> 1][8 * (j & 1) + e];
+              pf.hi[e] = s[j >> 1][8 * (j & 1) + 4 + e];
+            }
+          }
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            Frag<T> a;
+            load_vt(a, vl, V_LD, j, nb, lane);
+            mma(o_acc[nb], a, pf);
+          }
         }
       }
     }
+    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
   const size_t row = ((size_t)b * p.Hq + g) * p.S + qpos;
-  if (hf == 0) p.lse[row] = (l_run > 0.f) ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
+  if (hf == 0) p.lse[row] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   if constexpr (WITH_O) {
-    const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
+    const float inv_l = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     T *orow = reinterpret_cast<T *>(p.o) + row * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
