@@ -40,15 +40,19 @@ struct FwdParams {
   int list_cap, sinks, window;
 };
 
+#ifndef KVPOP_FWD_V_PAD
+#define KVPOP_FWD_V_PAD 64
+#endif
+
 template <typename T, int D>
 struct FwdTiles {
   static constexpr int KT = 64;                           // keys per tile
   static constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                     // 16-byte chunks per row
   static constexpr int K_BYTES = KT * D * (int)sizeof(T);
-  // V rows keep their natural layout, padded by 32 bytes so that the
-  // transposed 8-byte reads of four consecutive rows hit distinct banks.
-  static constexpr int V_LD = D * (int)sizeof(T) + 32;
+  // V rows keep their natural layout, padded so that the transposed 8-byte
+  // reads of four consecutive rows hit distinct banks.
+  static constexpr int V_LD = D * (int)sizeof(T) + KVPOP_FWD_V_PAD;
   static constexpr int V_BYTES = KT * V_LD;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int PER_THREAD = KT * CPR / 256;       // chunks of K (and of V) per thread

@@ -96,6 +96,10 @@ struct SwizzledTile {
   }
   // byte offset of chunk c of row r
   __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
+  // bf16 k-chunk stored at byte offset o (a value of off())
+  __device__ static __forceinline__ void read_at(Frag<bf16> &f, const char *base, int o) {
+    f.v = *reinterpret_cast<const bf16x8 *>(base + o);
+  }
   // k-chunk (8 elements starting at element e0, a multiple of 8) of row r
   __device__ static __forceinline__ void read(Frag<T> &f, const char *base, int r, int e0) {
     constexpr int kChunkElems = 16 / (int)sizeof(T);
@@ -123,6 +127,14 @@ __device__ __forceinline__ Doc find_doc(const int *cu, int n_docs, int S, int po
     if (__ldg(cu + mid) <= pos) lo = mid; else hi = mid - 1;
   }
   return Doc{__ldg(cu + lo), __ldg(cu + lo + 1)};
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor, no
+// swizzle, stride 0): a load at an offset >= bytes returns zero instead of
+// touching memory, so tile loads need no per-lane clamping.
+constexpr int kBufferDword3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferDword3);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -29,6 +29,8 @@
 //  * Blocks are ordered (batch, KV head, document, chunk descending, key tile)
 //    and dealt out so that each XCD (one L2) receives a contiguous range:
 //    concurrently running blocks of an XCD share the same query chunk.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -139,37 +141,53 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
 
   float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   u32x4 qreg[Q_PER_THREAD];
-  float nlreg = 0.f;
+  float lreg = 0.f;
+
+  // Per-thread byte offsets of its Q chunks inside a 32-row tile, and of the
+  // same chunks in the swizzled LDS tile; both are loop invariant.
+  int q_voff[Q_PER_THREAD], q_loff[Q_PER_THREAD];
+#pragma unroll
+  for (int cc = 0; cc < Q_PER_THREAD; ++cc) {
+    const int li = tid + 256 * cc;
+    const int rr = li / CPR, ch = li % CPR;
+    q_voff[cc] = (rr * D + ch * EPC) * (int)sizeof(T);
+    q_loff[cc] = QTile::off(rr, ch);
+  }
+  int a_off[NJ];  // bf16: this lane's A-operand chunks (query row `col`)
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) a_off[jj] = QTile::off(col, 2 * jj + hf);
+  auto read_a = [&](Frag<T> &a, const char *base, int jj) {
+    if constexpr (sizeof(T) == 2) QTile::read_at(a, base, a_off[jj]);
+    else QTile::read(a, base, col, 16 * jj + 8 * hf);
+  };
 
   auto q_of = [&](int it, int &gg, int &q0) {
     gg = it / n_sub;
     q0 = qs_al + 32 * (it % n_sub);
   };
+  // Loads query tile `it` (32 rows of one head) and its LSE into registers.
+  // The buffer ends at the document end, so rows past it read as zero; they
+  // are masked out below.
   auto prefetch = [&](int it) {
     int gg, q0;
     q_of(it, gg, q0);
     const int g = h * p.G + gg;
-    const T *qb = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + g) * (size_t)p.S * D;
+    const int rows = min(32, n - q0);
+    const size_t row0 = ((size_t)b * p.Hq + g) * p.S + dstart + q0;
+    const auto qr = make_rsrc(reinterpret_cast<const T *>(p.q) + row0 * D, rows * D * (int)sizeof(T));
 #pragma unroll
-    for (int c = 0; c < Q_PER_THREAD; ++c) {
-      const int li = tid + 256 * c;
-      const int rr = li / CPR, ch = li % CPR;
-      const int qrow = dstart + min(q0 + rr, n - 1);
-      qreg[c] = *reinterpret_cast<const u32x4 *>(qb + (size_t)qrow * D + ch * EPC);
-    }
+    for (int cc = 0; cc < Q_PER_THREAD; ++cc)
+      qreg[cc] = __builtin_amdgcn_raw_buffer_load_b128(qr, q_voff[cc], 0, 0);
     if (tid < 32) {
-      const int qrow = dstart + min(q0 + tid, n - 1);
-      nlreg = p.lse[((size_t)b * p.Hq + g) * p.S + qrow];
+      const auto lr = make_rsrc(p.lse + row0, rows * 4);
+      lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, tid * 4, 0, 0));
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int c = 0; c < Q_PER_THREAD; ++c) {
-      const int li = tid + 256 * c;
-      const int rr = li / CPR, ch = li % CPR;
-      *reinterpret_cast<u32x4 *>(q_lds[buf] + QTile::off(rr, ch)) = qreg[c];
-    }
-    if (tid < 32) nl_lds[buf][tid] = -nlreg * kLog2e;
+    for (int cc = 0; cc < Q_PER_THREAD; ++cc) *reinterpret_cast<u32x4 *>(q_lds[buf] + q_loff[cc]) = qreg[cc];
+    if (tid < 32) nl_lds[buf][tid] = -lreg * kLog2e;
   };
   auto write_partial = [&](int hp) {
     // the two lane halves hold complementary query rows of the same key
@@ -182,11 +200,11 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
       acc[cb][0] = acc[cb][1] = 0.f;
     }
   };
-
-  prefetch(0);
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    store(buf);
+  // One query tile: store the prefetched tile to LDS stage `buf`, start the
+  // next prefetch, then MFMA + exp2 + column sums on this stage.
+  auto step = [&](auto bufc, int it) {
+    constexpr int buf = decltype(bufc)::value;
+    store(bufc);
     __syncthreads();
     if (it + 1 < n_it) prefetch(it + 1);
 
@@ -205,14 +223,14 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
       f32x16 s[2];
       {
         Frag<T> a;
-        QTile::read(a, q_lds[buf], col, 8 * hf);
+        read_a(a, q_lds[buf], 0);
         s[0] = mma_add(a, kf[0][0], cadd);
         s[1] = mma_add(a, kf[1][0], cadd);
       }
 #pragma unroll
       for (int jj = 1; jj < NJ; ++jj) {
         Frag<T> a;
-        QTile::read(a, q_lds[buf], col, 16 * jj + 8 * hf);
+        read_a(a, q_lds[buf], jj);
         mma(s[0], a, kf[0][jj]);
         mma(s[1], a, kf[1][jj]);
       }
@@ -238,6 +256,12 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
     if constexpr (!SUM_HEADS) {
       if ((it + 1) % n_sub == 0) write_partial(h * p.G + gg);
     }
+  };
+
+  prefetch(0);
+  for (int it = 0; it < n_it; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
   }
   if constexpr (SUM_HEADS) write_partial(h);
 }
