@@ -59,6 +59,11 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libkvpop.so failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host stub was not emitted links fine but fails to load
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    missing = [ln.split()[-1] for ln in und.splitlines() if "kvpop" in ln]
+    if missing:
+        raise RuntimeError("libkvpop.so has undefined library symbols: " + ", ".join(missing[:8]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -11,9 +11,13 @@
 //  * A block is (batch row, KV head, document, key tile of 256 keys, query
 //    chunk of DT queries).  Its four waves each keep 64 keys of K resident in
 //    registers (the MFMA A operand) for the whole block.
-//  * Query tiles of 32 positions stream through double-buffered, swizzled
-//    LDS together with -L_d*log2(e); for every query head of the group each
-//    wave computes S = Q K'^T (32 queries x 64 keys) with MFMA.  K' is K
+//  * Query tiles of 64 positions stream through double-buffered, swizzled
+//    LDS together with -L_d*log2(e) (precomputed once per call by a small
+//    elementwise kernel).  The tiles are fetched by buffer loads that write
+//    straight into LDS, with the swizzle folded into each lane's source
+//    offset, so no registers or LDS stores are spent on staging.  For every
+//    query head of the group each wave computes S = Q K'^T (32 queries x 64
+//    keys per half tile) with MFMA.  K' is K
 //    multiplied by scale*log2(e) (rounded to the input type once per block)
 //    and the MFMA addend is -L_d*log2(e), so the accumulator is directly the
 //    exp2 argument: per element only exp2 and one add into the per-lane sum
@@ -40,7 +44,7 @@ constexpr int TGT_KT = 256;  // keys per block: 4 waves x 64
 
 struct TgtParams {
   const void *q, *k;
-  const float *lse;
+  const float *nl;  // -L*log2(e) per query, [B, Hq, S]
   float *part;
   int B, S, Hq, Hkv, G, window;
   float scale_log2;
@@ -62,19 +66,24 @@ __host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w) 
   return c;
 }
 
+// -L*log2(e) for every query: the MFMA addend of the target kernel.
+__global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, float *nl, size_t count) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) nl[i] = -lse[i] * kLog2e;
+}
+
 template <typename T, int D, bool SUM_HEADS>
-__global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) future_target_kernel(const TgtParams p) {
   using QTile = SwizzledTile<T, D>;
   constexpr int NJ = D / 16;
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = D / EPC;
-  constexpr int Q_PER_THREAD = 32 * CPR / 256;
-  static_assert(32 * CPR % 256 == 0, "Q tile must split over 256 threads");
-  constexpr int QBYTES = 32 * D * (int)sizeof(T);
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int QT = 64;                                // queries per LDS stage
+  constexpr int ROWB = D * (int)sizeof(T);              // bytes per query row
+  constexpr int QBYTES = QT * ROWB;
+  constexpr int LOADS = QBYTES / 1024 / 4;              // 1 KB direct loads per wave and stage
+  static_assert(QBYTES % 4096 == 0 && LOADS >= 1, "stage must split into 1 KB loads per wave");
 
   __shared__ __align__(16) char q_lds[2][QBYTES];
-  __shared__ __align__(16) float nl_lds[2][32];
+  __shared__ __align__(16) float nl_lds[2][QT];
 
   // ---- which block ----
   const int per_xcd = (p.total_blocks + 7) / 8;
@@ -132,27 +141,23 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
     }
   }
 
-  // ---- query sub-tiles of this chunk ----
+  // ---- query stages of this chunk: 64 rows each, from qs_al (32-aligned) ----
   const int cq0 = j * p.DT, cq1 = min(n, (j + 1) * p.DT);
   const int qs = max(cq0, t0 + w);
   const int qs_al = cq0 + ((qs - cq0) & ~31);
-  const int n_sub = (cq1 - qs_al + 31) / 32;
-  const int n_it = p.G * n_sub;
+  const int n_st = (cq1 - qs_al + QT - 1) / QT;
+  const int n_it = p.G * n_st;
 
   float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  u32x4 qreg[Q_PER_THREAD];
-  float lreg = 0.f;
 
-  // Per-thread byte offsets of its Q chunks inside a 32-row tile, and of the
-  // same chunks in the swizzled LDS tile; both are loop invariant.
-  int q_voff[Q_PER_THREAD], q_loff[Q_PER_THREAD];
-#pragma unroll
-  for (int cc = 0; cc < Q_PER_THREAD; ++cc) {
-    const int li = tid + 256 * cc;
-    const int rr = li / CPR, ch = li % CPR;
-    q_voff[cc] = (rr * D + ch * EPC) * (int)sizeof(T);
-    q_loff[cc] = QTile::off(rr, ch);
-  }
+  // Direct-to-LDS loads: load k of this wave fills LDS chunks
+  // [(wave*LOADS + k)*64, +64) of a stage, lane by lane.  Each lane fetches
+  // the global chunk that the swizzle places at its LDS chunk.
+  auto src_off = [&](int k) {
+    const int pch = (wave * LOADS + k) * 64 + lane;  // LDS chunk index in the stage
+    const int row = pch / QTile::kChunks, slot = pch % QTile::kChunks;
+    return row * ROWB + ((slot ^ QTile::swz(row)) << 4);
+  };
   int a_off[NJ];  // bf16: this lane's A-operand chunks (query row `col`)
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) a_off[jj] = QTile::off(col, 2 * jj + hf);
@@ -162,32 +167,23 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
   };
 
   auto q_of = [&](int it, int &gg, int &q0) {
-    gg = it / n_sub;
-    q0 = qs_al + 32 * (it % n_sub);
+    gg = it / n_st;
+    q0 = qs_al + QT * (it % n_st);
   };
-  // Loads query tile `it` (32 rows of one head) and its LSE into registers.
-  // The buffer ends at the document end, so rows past it read as zero; they
-  // are masked out below.
-  auto prefetch = [&](int it) {
+  // Starts the loads of stage `it` (64 rows of one head and their -L*log2e)
+  // into LDS buffer `buf`.  The buffers end at the document end, so rows past
+  // it arrive as zeros; they are masked out below.
+  auto fetch = [&](auto bufc, int it) {
+    constexpr int buf = decltype(bufc)::value;
     int gg, q0;
     q_of(it, gg, q0);
     const int g = h * p.G + gg;
-    const int rows = min(32, n - q0);
+    const int rows = min(QT, n - q0);
     const size_t row0 = ((size_t)b * p.Hq + g) * p.S + dstart + q0;
-    const auto qr = make_rsrc(reinterpret_cast<const T *>(p.q) + row0 * D, rows * D * (int)sizeof(T));
+    const auto qr = make_rsrc(reinterpret_cast<const T *>(p.q) + row0 * D, rows * ROWB);
 #pragma unroll
-    for (int cc = 0; cc < Q_PER_THREAD; ++cc)
-      qreg[cc] = __builtin_amdgcn_raw_buffer_load_b128(qr, q_voff[cc], 0, 0);
-    if (tid < 32) {
-      const auto lr = make_rsrc(p.lse + row0, rows * 4);
-      lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, tid * 4, 0, 0));
-    }
-  };
-  auto store = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-#pragma unroll
-    for (int cc = 0; cc < Q_PER_THREAD; ++cc) *reinterpret_cast<u32x4 *>(q_lds[buf] + q_loff[cc]) = qreg[cc];
-    if (tid < 32) nl_lds[buf][tid] = -lreg * kLog2e;
+    for (int k = 0; k < LOADS; ++k) lds_load16(qr, q_lds[buf] + (wave * LOADS + k) * 1024, src_off(k));
+    if (wave == 0) lds_load4(make_rsrc(p.nl + row0, rows * 4), nl_lds[buf], lane * 4);
   };
   auto write_partial = [&](int hp) {
     // the two lane halves hold complementary query rows of the same key
@@ -200,65 +196,68 @@ __global__ void __launch_bounds__(256) future_target_kernel(const TgtParams p) {
       acc[cb][0] = acc[cb][1] = 0.f;
     }
   };
-  // One query tile: store the prefetched tile to LDS stage `buf`, start the
-  // next prefetch, then MFMA + exp2 + column sums on this stage.
-  auto step = [&](auto bufc, int it) {
-    constexpr int buf = decltype(bufc)::value;
-    store(bufc);
-    __syncthreads();
-    if (it + 1 < n_it) prefetch(it + 1);
-
-    int gg, q0;
-    q_of(it, gg, q0);
-    const bool any = (q0 + 31 >= tw + w) && (tw < n);
-    if (any) {
-      // addend: -L*log2(e) of the query row held by each register
-      f32x16 cadd;
+  // One half stage: 32 query rows starting at row `h32` of the stage.
+  auto half = [&](const char *ql, const float *nl, int q0) {
+    // accumulators start at -L*log2(e) of the query row held by each
+    // register (read twice from LDS rather than kept in a third tile)
+    f32x16 s[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl_lds[buf][8 * i4 + 4 * hf]);
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl[8 * i4 + 4 * hf]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cadd[4 * i4 + e] = v4[e];
-      }
-      f32x16 s[2];
-      {
-        Frag<T> a;
-        read_a(a, q_lds[buf], 0);
-        s[0] = mma_add(a, kf[0][0], cadd);
-        s[1] = mma_add(a, kf[1][0], cadd);
+        for (int e = 0; e < 4; ++e) s[cb][4 * i4 + e] = v4[e];
       }
 #pragma unroll
-      for (int jj = 1; jj < NJ; ++jj) {
-        Frag<T> a;
-        read_a(a, q_lds[buf], jj);
-        mma(s[0], a, kf[0][jj]);
-        mma(s[1], a, kf[1][jj]);
-      }
-      const bool interior = (q0 >= tw + 63 + w) && (q0 + 31 < n) && (tw + 63 < n);
-      if (interior) {
+    for (int jj = 0; jj < NJ; ++jj) {
+      Frag<T> a;
+      read_a(a, ql, jj);
+      mma(s[0], a, kf[0][jj]);
+      mma(s[1], a, kf[1][jj]);
+    }
+    const bool interior = (q0 >= tw + 63 + w) && (q0 + 31 < n) && (tw + 63 < n);
+    if (interior) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i]);
-      } else {
+        for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i]);
+    } else {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int t = tw + 32 * cb + col;
+      for (int cb = 0; cb < 2; ++cb) {
+        const int t = tw + 32 * cb + col;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int d = q0 + c_row(i, hf);
-            const float pv = fast_exp2(s[cb][i]);
-            acc[cb][i & 1] += (d >= t + w && d < n && t < n) ? pv : 0.f;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int d = q0 + c_row(i, hf);
+          const float pv = fast_exp2(s[cb][i]);
+          acc[cb][i & 1] += (d >= t + w && d < n && t < n) ? pv : 0.f;
         }
       }
     }
+  };
+  // One stage: wait for this wave's loads of stage `it`, publish them with a
+  // barrier (which also retires every read of the other buffer), start the
+  // loads of stage it+1 into the other buffer, then compute on this one.
+  auto step = [&](auto bufc, int it) {
+    constexpr int buf = decltype(bufc)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < n_it) fetch(std::integral_constant<int, 1 - buf>{}, it + 1);
+
+    int gg, q0;
+    q_of(it, gg, q0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int qh = q0 + 32 * hh;
+      // the half must meet a key of this wave and lie inside the chunk
+      if (qh < cq1 && qh + 31 >= tw + w && tw < n) half(q_lds[buf] + 32 * hh * ROWB, nl_lds[buf] + 32 * hh, qh);
+    }
     if constexpr (!SUM_HEADS) {
-      if ((it + 1) % n_sub == 0) write_partial(h * p.G + gg);
+      if ((it + 1) % n_st == 0) write_partial(h * p.G + gg);
     }
   };
 
-  prefetch(0);
+  fetch(std::integral_constant<int, 0>{}, 0);
   for (int it = 0; it < n_it; it += 2) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
@@ -312,10 +311,15 @@ int tgt_chunk(int max_doc) {
   return 1024;
 }
 
-size_t tgt_workspace_bytes(const ShapeInfo &s) {
+// Workspace: per-chunk partial sums [B, Hq or Hkv, n_chunks, S], then the
+// scaled normaliser -L*log2(e) [B, Hq, S].
+static size_t tgt_partial_floats(const ShapeInfo &s) {
   const int DT = tgt_chunk(s.max_doc);
   const size_t nch_max = (size_t)((s.max_doc + DT - 1) / DT);
-  return (size_t)s.B * s.Hq * nch_max * s.S * sizeof(float);
+  return (size_t)s.B * s.Hq * nch_max * s.S;
+}
+size_t tgt_workspace_bytes(const ShapeInfo &s) {
+  return (tgt_partial_floats(s) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
 }
 
 template <typename T, int D, bool SUM>
@@ -330,8 +334,9 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   TgtParams tp{};
   tp.q = q;
   tp.k = k;
-  tp.lse = lse;
   tp.part = reinterpret_cast<float *>(ws);
+  float *nl = tp.part + tgt_partial_floats(s);
+  tp.nl = nl;
   tp.B = s.B;
   tp.S = s.S;
   tp.Hq = s.Hq;
@@ -356,6 +361,10 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.Hp = sum ? s.Hkv : s.Hq;
   hipError_t e = hipSuccess;
   if (tp.total_blocks > 0) {
+    const size_t count = (size_t)s.B * s.Hq * s.S;
+    hipLaunchKernelGGL(future_target_neg_lse, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, lse, nl,
+                       count);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int grid = 8 * ((tp.total_blocks + 7) / 8);
     if (s.dtype == 0 && s.D == 128) e = sum ? launch_tgt<bf16, 128, true>(tp, grid, st) : launch_tgt<bf16, 128, false>(tp, grid, st);
     else if (s.dtype == 0 && s.D == 64) e = sum ? launch_tgt<bf16, 64, true>(tp, grid, st) : launch_tgt<bf16, 64, false>(tp, grid, st);
