@@ -40,23 +40,23 @@ struct FwdParams {
   int list_cap, sinks, window;
 };
 
-#ifndef KVPOP_FWD_V_PAD
-#define KVPOP_FWD_V_PAD 64
-#endif
-
 template <typename T, int D>
 struct FwdTiles {
   static constexpr int KT = 64;                           // keys per tile
   static constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                     // 16-byte chunks per row
-  static constexpr int K_BYTES = KT * D * (int)sizeof(T);
-  // V rows keep their natural layout, padded so that the transposed 8-byte
-  // reads of four consecutive rows hit distinct banks.
-  static constexpr int V_LD = D * (int)sizeof(T) + KVPOP_FWD_V_PAD;
-  static constexpr int V_BYTES = KT * V_LD;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int ROWB = D * (int)sizeof(T);         // bytes per row
+  static constexpr int K_BYTES = KT * ROWB;
+  static constexpr int STAGE = 2 * K_BYTES;               // K tile, then V tile
   static constexpr int PER_THREAD = KT * CPR / 256;       // chunks of K (and of V) per thread
-  static_assert(KT * CPR % 256 == 0, "tile must split evenly over 256 threads");
+  static constexpr int LOADS = K_BYTES / 4096;            // 1 KB direct loads per wave and tensor
+  static_assert(KT * CPR % 256 == 0 && K_BYTES % 4096 == 0, "tile must split evenly over 4 waves");
+  // V rows keep their natural layout; 16-byte chunk c of row r sits at slot
+  // c ^ vswz(r), so that the transposed 8-byte reads of four consecutive
+  // rows (or two rows of the other bank half, for 128-byte rows) hit
+  // distinct banks.
+  __device__ static __forceinline__ int vswz(int r) { return ROWB >= 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __device__ static __forceinline__ int voff(int r, int c) { return r * ROWB + ((c ^ vswz(r)) << 4); }
 };
 
 // Rescaling of the running output is skipped until a row maximum grows by
@@ -66,29 +66,43 @@ constexpr float kLazyRescaleLog2 = 8.f;
 // A operand of O^T = V^T P^T for the 16-key step j and the 32 head-dim rows
 // of block nb: lane l needs V[keys 16j + 4*hf + {0..3} and 16j + 8 + 4*hf +
 // {0..3}][32*nb + l%32] (the key order of the P^T fragment).
-__device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int v_ld, int j, int nb, int lane) {
+//
+// ds_read_tr16_b64: within each group of 16 lanes, lane i returns element
+// i%4 of the 4-element (8-byte) pieces read by lanes i/4, i/4+4, i/4+8 and
+// i/4+12.  Lane jj of a group therefore reads row k0 + jj/4 at columns
+// d0 + 4*(jj%4).  With the V swizzle the byte offset of that piece is
+//   16*ROWB*j + (4*hf + x)*ROWB + 64*(nb ^ y) + 32*grp + 8*(jj%4)
+// (x = jj/4, y = the swizzle bits of x), plus 8*ROWB for keys 8..15 of the
+// step: vt_off() gives the per-lane part for each nb once, the rest are
+// immediates.
+template <int ROWB>
+__device__ __forceinline__ int vt_off(int lane, int nb) {
+  const int hf = lane >> 5, grp = (lane >> 4) & 1, jj = lane & 15, x = jj >> 2;
+  const int y = ROWB >= 256 ? x : ((x >> 1) & 1);
+  return (4 * hf + x) * ROWB + 64 * (nb ^ y) + 32 * grp + 8 * (jj & 3);
+}
+template <int ROWB>
+__device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int off_nb, int j, int, int) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  // ds_read_tr16_b64: within each group of 16 lanes, lane i returns element
-  // i%4 of the 4-element chunks read by lanes i/4, i/4+4, i/4+8 and i/4+12.
-  // Lane jj of a group therefore reads row k0 + jj/4, columns d0 + 4*(jj%4).
-  const int hf = lane >> 5, grp = (lane >> 4) & 1, jj = lane & 15;
-  const int row = 16 * j + 4 * hf + (jj >> 2);
-  const int colb = 2 * (32 * nb + 16 * grp + 4 * (jj & 3));
-  const char *p0 = vl + row * v_ld + colb;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)(p0 + 8 * v_ld));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char *p0 = vl + off_nb + 16 * ROWB * j;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)(p0 + 8 * ROWB));
   const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   a.v = __builtin_bit_cast(bf16x8, w);
 }
-__device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int v_ld, int j, int nb, int lane) {
+// fp32 V (correctness path): eight scalar reads through the swizzle.
+template <int ROWB>
+__device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int, int j, int nb, int lane) {
+  using Tl = FwdTiles<float, ROWB / 4>;
   const int hf = lane >> 5, d = 32 * nb + (lane & 31);
-  const float *c0 = reinterpret_cast<const float *>(vl + (16 * j + 4 * hf) * v_ld) + d;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    a.lo[e] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(c0) + e * v_ld);
-    a.hi[e] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(c0) + (8 + e) * v_ld);
+    const int r0 = 16 * j + 4 * hf + e, r1 = r0 + 8;
+    a.lo[e] = *reinterpret_cast<const float *>(vl + Tl::voff(r0, d >> 2) + 4 * (d & 3));
+    a.hi[e] = *reinterpret_cast<const float *>(vl + Tl::voff(r1, d >> 2) + 4 * (d & 3));
   }
 }
 
@@ -102,7 +116,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   constexpr int EPC = Tiles::EPC;
   constexpr int CPR = Tiles::CPR;
   constexpr int PT = Tiles::PER_THREAD;
-  constexpr int V_LD = Tiles::V_LD;
+  constexpr int ROWB = Tiles::ROWB;
+  constexpr int LOADS = Tiles::LOADS;
 
   // two stages of (K tile, V tile): one barrier per tile
   __shared__ __align__(16) char smem[2][Tiles::STAGE];
@@ -167,8 +182,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   const float c = p.scale_log2;
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 kreg[PT], vreg[PT];
+  // register staging: only the budget-masked path, whose keys are gathered
+  u32x4 kreg[SPARSE ? PT : 1], vreg[SPARSE ? PT : 1];
   int my_kpos = INT32_MAX, my_krank = 0;
+  int vt_base[NB];  // per-lane part of the transposed V reads
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) vt_base[nb] = vt_off<ROWB>(lane, nb);
 
   auto key_of = [&](int tile, int r, bool &valid) -> int {
     if constexpr (!SPARSE) {
@@ -184,46 +203,77 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  auto prefetch = [&](int tile) {
+  // Dense keys are contiguous: each wave issues LOADS buffer loads of 1 KB
+  // per tensor that write straight into the LDS stage (lane l at +16*l), the
+  // swizzles folded into each lane's source offset.  Rows past kend arrive
+  // as zeros (they are masked anyway).
+  auto fetch_dense = [&](int tile, int buf) {
+    const int tb = kbeg + tile * KT;
+    const int rows = min(KT, kend - tb);
+    const auto kr = make_rsrc(kbase + (size_t)tb * D, rows * ROWB);
+    const auto vr = make_rsrc(vbase + (size_t)tb * D, rows * ROWB);
 #pragma unroll
-    for (int cc = 0; cc < PT; ++cc) {
-      const int li = tid + 256 * cc;
-      const int r = li / CPR, ch = li % CPR;
-      bool valid;
-      const int t = key_of(tile, r, valid);
-      kreg[cc] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)t * D + ch * EPC);
-      vreg[cc] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)t * D + ch * EPC);
+    for (int k = 0; k < LOADS; ++k) {
+      const int pch = (wave * LOADS + k) * 64 + lane;  // chunk position in the tile
+      const int r = pch / CPR, slot = pch % CPR;
+      lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, r * ROWB + ((slot ^ KTile::swz(r)) << 4));
+      lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024,
+                 r * ROWB + ((slot ^ Tiles::vswz(r)) << 4));
     }
-    if (tid < KT) {
-      bool valid;
-      const int t = key_of(tile, tid, valid);
-      my_kpos = valid ? t : INT32_MAX;
-      if constexpr (SPARSE) my_krank = valid ? p.rank[bh_kv * p.S + t] : INT32_MAX;
+  };
+
+  auto prefetch = [&](int tile) {
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int cc = 0; cc < PT; ++cc) {
+        const int li = tid + 256 * cc;
+        const int r = li / CPR, ch = li % CPR;
+        bool valid;
+        const int t = key_of(tile, r, valid);
+        kreg[cc] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)t * D + ch * EPC);
+        vreg[cc] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)t * D + ch * EPC);
+      }
+      if (tid < KT) {
+        bool valid;
+        const int t = key_of(tile, tid, valid);
+        my_kpos = valid ? t : INT32_MAX;
+        my_krank = valid ? p.rank[bh_kv * p.S + t] : INT32_MAX;
+      }
     }
   };
 
   auto store_tile = [&](int buf) {
+    if constexpr (SPARSE) {
 #pragma unroll
-    for (int cc = 0; cc < PT; ++cc) {
-      const int li = tid + 256 * cc;
-      const int r = li / CPR, ch = li % CPR;
-      *reinterpret_cast<u32x4 *>(smem[buf] + KTile::off(r, ch)) = kreg[cc];
-      *reinterpret_cast<u32x4 *>(smem[buf] + Tiles::K_BYTES + r * V_LD + 16 * ch) = vreg[cc];
-    }
-    if (tid < KT) {
-      kpos_lds[buf][tid] = my_kpos;
-      krank_lds[buf][tid] = my_krank;
+      for (int cc = 0; cc < PT; ++cc) {
+        const int li = tid + 256 * cc;
+        const int r = li / CPR, ch = li % CPR;
+        *reinterpret_cast<u32x4 *>(smem[buf] + KTile::off(r, ch)) = kreg[cc];
+        *reinterpret_cast<u32x4 *>(smem[buf] + Tiles::K_BYTES + Tiles::voff(r, ch)) = vreg[cc];
+      }
+      if (tid < KT) {
+        kpos_lds[buf][tid] = my_kpos;
+        krank_lds[buf][tid] = my_krank;
+      }
     }
   };
 
   if (n_tiles > 0) {
-    prefetch(0);
-    store_tile(0);
+    if constexpr (SPARSE) {
+      prefetch(0);
+      store_tile(0);
+    } else {
+      fetch_dense(0, 0);
+    }
   }
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
+    if constexpr (!SPARSE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tile + 1 < n_tiles) prefetch(tile + 1);
+    if (tile + 1 < n_tiles) {
+      if constexpr (SPARSE) prefetch(tile + 1);
+      else fetch_dense(tile + 1, buf ^ 1);
+    }
 
     // Which of this wave's elements can be valid in this tile?
     bool any = wave_active, full = false;
@@ -312,13 +362,15 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             Frag<T> a;
-            load_vt(a, vl, V_LD, j, nb, lane);
+            load_vt<ROWB>(a, vl, vt_base[nb], j, nb, lane);
             mma(o_acc[nb], a, pf);
           }
         }
       }
     }
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+    if constexpr (SPARSE) {
+      if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
