@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "future-attention target keys/s + TFLOP/s (% bf16 MFMA peak) at S=16384"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stack36.json")
+CSRC = os.path.join(ROOT, "attention_target_amd", "csrc")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 
@@ -66,12 +68,43 @@ def cpu_baseline(q, k, v, window, budget_s: float = 20.0):
             "seconds": dt}
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter readings taken on other sources do not apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
+    copy of known size), or None when the sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or kernel_key not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel_key]
+    return round(k["fetch_kib"] * 1024 * t["fetch_factor"] + k["write_kib"] * 1024 * t["write_factor"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="profiling runs only: fewer resident layers (the reported line is then not the metric)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="profiling runs only: finish with a plain device copy of this many MiB, the "
+                         "reference reading for the FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no collectives: "
@@ -88,6 +121,8 @@ def main():
     spec = synth.WORKLOADS["stack36"]
     L, B, S, Hq, Hkv, D, w = spec.layers, spec.batch, spec.seqlen, spec.n_q_heads, spec.n_kv_heads, \
         spec.head_dim, spec.window
+    if args.layers is not None:
+        L = max(1, min(L, args.layers))
     layers = []
     for layer in range(L):
         t = synth.make_workload("stack36", layer=layer, device=dev)
@@ -143,13 +178,14 @@ def main():
     fwd_tflops = fwd_flop / (fwd_avg * 1e-3) / 1e12
     step_tflops = L * (tgt_flop + fwd_flop) / (ms_per_step * 1e-3) / 1e12
 
-    def roof(name, flop, ms, tflops):
+    def roof(name, key, flop, ms, tflops):
         return {"kernel": name, "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(key),
                 "flop_per_launch": flop, "avg_launch_ms": round(ms, 4)}
 
-    r_tgt = roof("future_target (kvpop_future_target)", tgt_flop, tgt_avg, tgt_tflops)
-    r_fwd = roof("attn_fwd (kvpop_attn_fwd_lse)", fwd_flop, fwd_avg, fwd_tflops)
+    r_tgt = roof("future_target_kernel (kvpop_future_target)", "future_target_kernel", tgt_flop, tgt_avg,
+                 tgt_tflops)
+    r_fwd = roof("attn_fwd_kernel (kvpop_attn_fwd_lse)", "attn_fwd_kernel", fwd_flop, fwd_avg, fwd_tflops)
     dominant = r_fwd if fwd_avg >= tgt_avg else r_tgt
 
     out = {
@@ -177,8 +213,17 @@ def main():
         "roofline": dominant,
         "kernels": {"future_target": r_tgt, "attn_fwd": r_fwd},
     }
+    if args.layers is not None:
+        out["config"]["layers"] = L
+        out["config"]["workload"] += f" [profiling run: {L} layers only]"
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 
