@@ -34,7 +34,8 @@ struct FwdParams {
   int n_docs;
   // budget-masked mode
   const int *lists;     // [B*Hkv][nqb][list_cap] key positions, ascending
-  const int *list_len;  // [B*Hkv][nqb]
+  const int *list_len;       // [B*Hkv][nqb]
+  const int *list_len_full;  // [B*Hkv][nqb]: leading entries kept by every query of the block
   const int *rank;      // [B*Hkv][S]
   const int *cutoff;    // [B*Hkv][S]
   int list_cap, sinks, window;
@@ -152,7 +153,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   for (int j = 0; j < NJ; ++j) load_frag(qf[j], qrow + 16 * j + 8 * hf);
 
   // Key range.
-  int kbeg = 0, kend = 0, n_tiles = 0, list_len = 0;
+  int kbeg = 0, kend = 0, n_tiles = 0, list_len = 0, full_tiles = 0;
   const int *list = nullptr;
   int wq_last = 0, wds_first = 0, wds_last = 0, qdoc_start = 0, cut_q = 0;
   if constexpr (!SPARSE) {
@@ -170,6 +171,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     list = p.lists + tile_id * p.list_cap;
     list_len = min(p.list_len[tile_id], p.list_cap);
     n_tiles = (list_len + KT - 1) / KT;
+    full_tiles = min(p.list_len_full[tile_id], list_len) / KT;
     cut_q = p.cutoff[bh_kv * p.S + qc];
   }
 
@@ -281,6 +283,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     if constexpr (!SPARSE) {
       any = any && tb <= wq_last && tb + KT - 1 >= wds_first;
       full = tb >= wds_last && tb + KT - 1 <= q0 && tb + KT - 1 < kend;
+    } else {
+      full = tile < full_tiles;
     }
     if (any) {
       const char *kl = smem[buf];

@@ -19,10 +19,12 @@
 //               (bitvectors + per-word prefix counts) by stable partitions;
 //   5. cutoff:  c_d for every d (KVPOP_CUTOFF_ALL when |E_d| < k, _NONE when
 //               k = 0);
-//   6. lists:   per query block [d0, d1] the ascending union of the keys any
-//               of its queries may keep: [0, s) below the window, the eligible
-//               tokens of [s, d0-w] with rank <= c_{d0}, and (d0-w, d1];
-//   7. forward: attention over the listed keys with per-element membership
+//   6. lists:   per query block [d0, d1] the union of the keys any of its
+//               queries may keep: [0, s) below the window, the eligible
+//               tokens of [s, d0-w] with rank <= c_{d0}, and (d0-w, d1], with
+//               the keys that every query of the block keeps listed first;
+//   7. forward: attention over the listed keys; tiles of the shared part
+//               need no mask, the rest use the per-element membership
 //               t <= d and (t < s or t > d-w or rank(t) <= c_d).
 #include "attn_fwd.h"
 #include "launch.h"
@@ -34,7 +36,7 @@ constexpr int CUT_ALL = 2147483647;
 constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
-  size_t keys, sorted, rank, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, total;
+  size_t keys, sorted, rank, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
 
@@ -71,6 +73,7 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   lo.zeros = take(BH * lo.L * 4);
   lo.lists = take(BH * lo.nqb * (size_t)lo.cap * 4);
   lo.lens = take(BH * lo.nqb * 4);
+  lo.lens_full = take(BH * lo.nqb * 4);
   lo.total = off;
   return lo;
 }
@@ -273,42 +276,90 @@ __global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int
 
 struct ListParams {
   const int *rank, *cutoff;
-  int *lists, *lens;
-  int S, sinks, window, QB, nqb, cap;
+  int *lists, *lens, *lens_full;
+  int S, sinks, window, topk, QB, nqb, cap;
 };
 
+// Key list of query block [d0, d1], in two ascending segments:
+//   full:    the sinks below the window, then the eligible tokens of
+//            [s, d0-w] with rank <= c_{d1}.  Every query of the block keeps
+//            all of them (c_d is non-increasing, so c_{d1} <= c_d), so
+//            their tiles need no per-element mask;
+//   partial: the eligible tokens with c_{d1} < rank <= c_{d0}, then the
+//            window region (d0-w, d1]; these are masked per element.
+// The size of the full segment is known before the sweep: E_{d1} holds
+// exactly topk tokens of rank <= c_{d1}, so E_{d0} holds topk minus those in
+// (d0-w, d1-w] (at most QB-1 reads).
 __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
-  __shared__ int sh_w[4];
+  __shared__ int sh_w[2][4];
+  __shared__ int sh_sub;
   const int qb = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d0 = qb * p.QB, d1 = min(p.S - 1, d0 + p.QB - 1);
   const int c0 = p.cutoff[bh * p.S + d0];
+  const int c1 = p.cutoff[bh * p.S + d1];
+  const int *rk = p.rank + bh * p.S;
   int *list = p.lists + (bh * p.nqb + qb) * (size_t)p.cap;
   const int a_end = max(0, min(min(p.sinks, d0 - p.window + 1), d1 + 1));
+  const int b_hi = d0 - p.window;  // E_{d0} = [sinks, b_hi]
+  const int n_e0 = max(0, b_hi - p.sinks + 1);
+  int n_bfull;
+  if (c1 == CUT_NONE) {
+    n_bfull = 0;
+  } else if (c1 == CUT_ALL) {
+    n_bfull = n_e0;
+  } else {
+    if (tid == 0) sh_sub = 0;
+    __syncthreads();
+    const int lo = max(p.sinks, b_hi + 1), hi = d1 - p.window;  // E_{d1} \ E_{d0}
+    const int t = lo + tid;
+    if (t <= hi && rk[t] <= c1) atomicAdd(&sh_sub, 1);  // LDS counter, at most QB-1 increments
+    __syncthreads();
+    n_bfull = p.topk - sh_sub;
+  }
+  const int n_full = a_end + n_bfull;
   for (int i = tid; i < a_end && i < p.cap; i += 256) list[i] = i;
-  int off = a_end;
-  const int b_hi = d0 - p.window;
+  int off_f = a_end, off_p = n_full;
   for (int base = p.sinks; base <= b_hi; base += 256) {
     const int t = base + tid;
-    const bool f = (t <= b_hi) && (p.rank[bh * p.S + t] <= c0);
-    const uint64_t m = __ballot(f);
-    if (lane == 0) sh_w[wave] = __popcll(m);
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) before += sh_w[w];
-      tot += sh_w[w];
+    const int r = (t <= b_hi) ? rk[t] : INT32_MAX;
+    const bool ff = (t <= b_hi) && r <= c1;
+    const bool fp = (t <= b_hi) && r > c1 && r <= c0;
+    const uint64_t mf = __ballot(ff), mp = __ballot(fp);
+    if (lane == 0) {
+      sh_w[0][wave] = __popcll(mf);
+      sh_w[1][wave] = __popcll(mp);
     }
-    const int slot = off + before + __popcll(m & lanemask_lt(lane));
-    if (f && slot < p.cap) list[slot] = t;
-    off += tot;
+    __syncthreads();
+    int bf = 0, bp = 0, tf = 0, tp = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) {
+        bf += sh_w[0][w];
+        bp += sh_w[1][w];
+      }
+      tf += sh_w[0][w];
+      tp += sh_w[1][w];
+    }
+    if (ff) {
+      const int slot = off_f + bf + __popcll(mf & lanemask_lt(lane));
+      if (slot < p.cap) list[slot] = t;
+    }
+    if (fp) {
+      const int slot = off_p + bp + __popcll(mp & lanemask_lt(lane));
+      if (slot < p.cap) list[slot] = t;
+    }
+    off_f += tf;
+    off_p += tp;
     __syncthreads();
   }
   const int c_lo = max(0, d0 - p.window + 1);
   const int n_c = d1 - c_lo + 1;
-  for (int i = tid; i < n_c && off + i < p.cap; i += 256) list[off + i] = c_lo + i;
-  if (tid == 0) p.lens[bh * p.nqb + qb] = min(off + n_c, p.cap);
+  for (int i = tid; i < n_c && off_p + i < p.cap; i += 256) list[off_p + i] = c_lo + i;
+  if (tid == 0) {
+    p.lens[bh * p.nqb + qb] = min(off_p + n_c, p.cap);
+    p.lens_full[bh * p.nqb + qb] = min(off_f, p.cap);
+  }
 }
 
 template <typename T, int D>
@@ -356,6 +407,8 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   lp.cutoff = cutoff;
   lp.lists = reinterpret_cast<int *>(w + lo.lists);
   lp.lens = reinterpret_cast<int *>(w + lo.lens);
+  lp.lens_full = reinterpret_cast<int *>(w + lo.lens_full);
+  lp.topk = topk;
   lp.S = s.S;
   lp.sinks = sinks;
   lp.window = window;
@@ -383,6 +436,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   fp.n_docs = 1;
   fp.lists = lp.lists;
   fp.list_len = lp.lens;
+  fp.list_len_full = lp.lens_full;
   fp.rank = rank;
   fp.cutoff = cutoff;
   fp.list_cap = lo.cap;
