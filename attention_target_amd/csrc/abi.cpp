@@ -169,6 +169,9 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
   if (s.cu != nullptr) return fail(KVPOP_EUNSUPPORTED, "the budget mask does not support packed sequences");
   if (s.dtype == KVPOP_F32 && s.D != 64)
     return fail(KVPOP_EUNSUPPORTED, "the fp32 budget forward supports head_dim 64 only");
+  if ((long long)s.S * s.D * (s.dtype == KVPOP_F32 ? 4 : 2) >= (1ll << 31))
+    return fail(KVPOP_EUNSUPPORTED, "the budget forward gathers keys with 32-bit offsets: seqlen * head_dim * "
+                                    "element size must stay below 2^31 bytes");
   const size_t need = kvpop::budget_workspace_bytes(s, sinks, window, topk);
   if (workspace == nullptr || ws_bytes < need)
     return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);

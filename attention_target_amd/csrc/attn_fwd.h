@@ -49,7 +49,6 @@ struct FwdTiles {
   static constexpr int ROWB = D * (int)sizeof(T);         // bytes per row
   static constexpr int K_BYTES = KT * ROWB;
   static constexpr int STAGE = 2 * K_BYTES;               // K tile, then V tile
-  static constexpr int PER_THREAD = KT * CPR / 256;       // chunks of K (and of V) per thread
   static constexpr int LOADS = K_BYTES / 4096;            // 1 KB direct loads per wave and tensor
   static_assert(KT * CPR % 256 == 0 && K_BYTES % 4096 == 0, "tile must split evenly over 4 waves");
   // V rows keep their natural layout; 16-byte chunk c of row r sits at slot
@@ -116,7 +115,6 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   constexpr int KT = Tiles::KT;
   constexpr int EPC = Tiles::EPC;
   constexpr int CPR = Tiles::CPR;
-  constexpr int PT = Tiles::PER_THREAD;
   constexpr int ROWB = Tiles::ROWB;
   constexpr int LOADS = Tiles::LOADS;
 
@@ -183,27 +181,13 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  // register staging: only the budget-masked path, whose keys are gathered
-  u32x4 kreg[SPARSE ? PT : 1], vreg[SPARSE ? PT : 1];
-  int my_kpos = INT32_MAX, my_krank = 0;
+  // budget-masked path: the key positions of this lane's rows of the next
+  // tile's gathers (loaded one tile ahead), and of row `tid` for the mask
+  int kidx[SPARSE ? LOADS : 1];
+  int next_kpos = INT32_MAX, my_kpos = INT32_MAX, my_krank = 0;
   int vt_base[NB];  // per-lane part of the transposed V reads
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) vt_base[nb] = vt_off<ROWB>(lane, nb);
-
-  auto key_of = [&](int tile, int r, bool &valid) -> int {
-    if constexpr (!SPARSE) {
-      const int t = kbeg + tile * KT + r;
-      valid = t < kend;
-      return valid ? t : kbeg;
-    } else {
-      const int idx = tile * KT + r;
-      valid = idx < list_len;
-      const int t = valid ? list[idx] : 0;
-      valid = valid && t >= 0 && t < p.S;
-      return valid ? t : 0;
-    }
-  };
 
   // Dense keys are contiguous: each wave issues LOADS buffer loads of 1 KB
   // per tensor that write straight into the LDS stage (lane l at +16*l), the
@@ -224,35 +208,46 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  auto prefetch = [&](int tile) {
+  // Gathered keys: the same direct-to-LDS loads, each lane's source row
+  // taken from the list (positions loaded a tile earlier by load_keys).
+  // Rows past the list end get an offset beyond the buffer and arrive as
+  // zeros.  The buffers span the whole (batch, KV head) sequence.
+  auto load_keys = [&](int tile) {
     if constexpr (SPARSE) {
 #pragma unroll
-      for (int cc = 0; cc < PT; ++cc) {
-        const int li = tid + 256 * cc;
-        const int r = li / CPR, ch = li % CPR;
-        bool valid;
-        const int t = key_of(tile, r, valid);
-        kreg[cc] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)t * D + ch * EPC);
-        vreg[cc] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)t * D + ch * EPC);
+      for (int k = 0; k < LOADS; ++k) {
+        const int r = ((wave * LOADS + k) * 64 + lane) / CPR;
+        const int idx = tile * KT + r;
+        const int t = (idx < list_len) ? list[idx] : -1;
+        kidx[k] = (t >= 0 && t < p.S) ? t : -1;
       }
       if (tid < KT) {
-        bool valid;
-        const int t = key_of(tile, tid, valid);
-        my_kpos = valid ? t : INT32_MAX;
-        my_krank = valid ? p.rank[bh_kv * p.S + t] : INT32_MAX;
+        const int idx = tile * KT + tid;
+        const int t = (idx < list_len) ? list[idx] : -1;
+        next_kpos = (t >= 0 && t < p.S) ? t : INT32_MAX;
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
+  auto fetch_sparse = [&](int buf) {
     if constexpr (SPARSE) {
+      const auto kr = make_rsrc(kbase, p.S * ROWB);
+      const auto vr = make_rsrc(vbase, p.S * ROWB);
 #pragma unroll
-      for (int cc = 0; cc < PT; ++cc) {
-        const int li = tid + 256 * cc;
-        const int r = li / CPR, ch = li % CPR;
-        *reinterpret_cast<u32x4 *>(smem[buf] + KTile::off(r, ch)) = kreg[cc];
-        *reinterpret_cast<u32x4 *>(smem[buf] + Tiles::K_BYTES + Tiles::voff(r, ch)) = vreg[cc];
+      for (int k = 0; k < LOADS; ++k) {
+        const int pch = (wave * LOADS + k) * 64 + lane;
+        const int r = pch / CPR, slot = pch % CPR;
+        const int row = kidx[k] >= 0 ? kidx[k] * ROWB : 0x7fff0000;
+        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + ((slot ^ KTile::swz(r)) << 4));
+        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + ((slot ^ Tiles::vswz(r)) << 4));
       }
+      if (tid < KT) {
+        my_kpos = next_kpos;
+        my_krank = my_kpos != INT32_MAX ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
+      }
+    }
+  };
+  auto store_pos = [&](int buf) {
+    if constexpr (SPARSE) {
       if (tid < KT) {
         kpos_lds[buf][tid] = my_kpos;
         krank_lds[buf][tid] = my_krank;
@@ -262,19 +257,25 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
 
   if (n_tiles > 0) {
     if constexpr (SPARSE) {
-      prefetch(0);
-      store_tile(0);
+      load_keys(0);
+      fetch_sparse(0);
+      store_pos(0);
+      if (n_tiles > 1) load_keys(1);
     } else {
       fetch_dense(0, 0);
     }
   }
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
-    if constexpr (!SPARSE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tile + 1 < n_tiles) {
-      if constexpr (SPARSE) prefetch(tile + 1);
-      else fetch_dense(tile + 1, buf ^ 1);
+      if constexpr (SPARSE) {
+        fetch_sparse(buf ^ 1);  // key positions loaded during the previous tile
+        if (tile + 2 < n_tiles) load_keys(tile + 2);
+      } else {
+        fetch_dense(tile + 1, buf ^ 1);
+      }
     }
 
     // Which of this wave's elements can be valid in this tile?
@@ -373,7 +374,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
       }
     }
     if constexpr (SPARSE) {
-      if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+      if (tile + 1 < n_tiles) store_pos(buf ^ 1);
     }
   }
 

@@ -136,7 +136,9 @@ kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const 
  * sparse normaliser the paper reuses for its target).  A row with nothing
  * kept (sinks = window = topk = 0) gets lse = -inf and O = 0.
  *
- *  q, k, v                          inputs as for kvpop_attn_fwd_lse (cu_seqlens must be NULL)
+ *  q, k, v                          inputs as for kvpop_attn_fwd_lse (cu_seqlens must be NULL;
+ *                                   seqlen * head_dim * element size < 2^31 bytes, else
+ *                                   KVPOP_EUNSUPPORTED)
  *  scores [B,Hkv,S] fp32            static priorities
  *  sinks, window, topk >= 0
  *  o [B,Hq,S,D] (dtype), lse [B,Hq,S] fp32   outputs
