@@ -16,7 +16,8 @@
 //   2. sort:    2048-key chunks sorted in LDS (bitonic);
 //   3. rank:    rank(t) = sum over chunks of the number of smaller keys;
 //   4. wavelet: one workgroup per (batch, KV head) builds the log2(S) levels
-//               (bitvectors + per-word prefix counts) by stable partitions;
+//               (bitvectors + per-word prefix counts) by stable partitions,
+//               inside LDS when the eligible range fits (32768 tokens);
 //   5. cutoff:  c_d for every d (KVPOP_CUTOFF_ALL when |E_d| < k, _NONE when
 //               k = 0);
 //   6. lists:   per query block [d0, d1] the union of the keys any of its
@@ -237,6 +238,72 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build(const WaveletParams
   }
 }
 
+// The same levels built inside LDS when the eligible range fits: the two
+// arrangements (16-bit ranks) and the level's bit words stay on chip, and
+// only the bit words, prefix counts and zero counts go to global memory.
+constexpr int WV_LDS_MAX = 32768;  // eligible tokens per (batch, KV head)
+constexpr int WV_LDS_WORDS = WV_LDS_MAX / 32 + 32;
+
+__global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletParams p) {
+  __shared__ uint16_t arr[2][WV_LDS_MAX];
+  __shared__ uint32_t wl[WV_LDS_WORDS];
+  __shared__ int pl_s[WV_LDS_WORDS];
+  __shared__ int sh_waves[16];
+  const size_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_e = p.S - p.sinks;
+  if (n_e <= 0 || n_e > WV_LDS_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
+  for (int i = tid; i < n_e; i += 1024) arr[0][i] = (uint16_t)p.rank[bh * p.S + p.sinks + i];
+  __syncthreads();
+  const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
+  int cur = 0;
+  for (int lvl = p.L - 1; lvl >= 0; --lvl) {
+    const uint16_t *a = arr[cur];
+    uint16_t *b = arr[cur ^ 1];
+    uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+    int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+    // bit words: one ballot gives the two words of 64 consecutive elements
+    for (int base = 0; base < 32 * p.nw1; base += 1024) {
+      const int i = base + tid;
+      const int bit = (i < n_e) ? ((a[i] >> lvl) & 1) : 0;
+      const uint64_t m = __ballot(bit);
+      const int w0 = (base + 64 * wave) / 32;
+      if (lane == 0 && w0 < p.nw1) wl[w0] = (uint32_t)m;
+      if (lane == 0 && w0 + 1 < p.nw1) wl[w0 + 1] = (uint32_t)(m >> 32);
+    }
+    __syncthreads();
+    int local = 0;
+    for (int q = 0; q < wpt; ++q) {
+      const int w = tid * wpt + q;
+      if (w < p.nw1) local += __popc(wl[w]);
+    }
+    int ones;
+    int run = block_excl_scan_1024(local, sh_waves, ones);
+    for (int q = 0; q < wpt; ++q) {
+      const int w = tid * wpt + q;
+      if (w < p.nw1) {
+        pl_s[w] = run;
+        pl[w] = run;
+        bl[w] = wl[w];
+        run += __popc(wl[w]);
+      }
+    }
+    const int Z = n_e - ones;
+    if (tid == 0) p.zeros[bh * p.L + lvl] = Z;
+    __syncthreads();
+    // stable partition: zeros first, then ones
+    for (int i = tid; i < n_e; i += 1024) {
+      const int v = a[i];
+      const int w = i >> 5;
+      const int before = pl_s[w] + __popc(wl[w] & ((1u << (i & 31)) - 1u));
+      const int pos = ((v >> lvl) & 1) ? Z + before : i - before;
+      if (pos >= 0 && pos < n_e) b[pos] = (uint16_t)v;
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+}
+
 __global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int window, int topk, int *cutoff) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   const size_t bh = blockIdx.y;
@@ -396,8 +463,12 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   wp.sinks = sinks;
   wp.L = lo.L;
   wp.nw1 = lo.nw1;
-  if (topk > 0 && s.S - sinks > 0)
-    hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
+  if (topk > 0 && s.S - sinks > 0) {
+    if (s.S - sinks <= WV_LDS_MAX && s.S <= 65536 && lo.nw1 <= WV_LDS_WORDS)
+      hipLaunchKernelGGL(budget_wavelet_build_lds, dim3(BH), dim3(1024), 0, st, wp);
+    else
+      hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
+  }
   hipLaunchKernelGGL(budget_cutoffs, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, wp, window, topk, cutoff);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
