@@ -68,6 +68,43 @@ def cpu_baseline(q, k, v, window, budget_s: float = 20.0):
             "seconds": dt}
 
 
+def budget_measurement(kv, synth, dev, reps: int = 10):
+    """Auxiliary (not part of `value`): the fixed-budget sparse forward on the
+    S=32768 budget workload (sinks 4, window 128, top-k 1916 -> B = 2048):
+    rank/cutoff construction, key lists and the masked attention, timed per
+    call with HIP events on the launch stream."""
+    t = synth.make_workload("budget32k", device=dev)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    s_, w_, k_ = t["sinks"], t["window"], t["topk"]
+    B_, Hq, S, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B_, Hq, S, dtype=torch.float32, device=dev)
+    ws = torch.empty(kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=s_, window=w_, topk=k_),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(reps + 3):
+        e0.record(stream)
+        kv.budget_mask_fwd(q, k, v, sc, s_, w_, k_, return_rank_cutoff=False, out=o, lse=lse, workspace=ws,
+                           stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    budget = s_ + w_ + k_
+    kept = sum(min(d + 1, budget) for d in range(S))          # kept (query, key) pairs per query head
+    flop = 4 * D * Hq * B_ * kept
+    return {"workload": f"budget32k: B={B_}, S={S}, {Hq}q/{k.shape[1]}kv heads, head_dim {D}, bf16; "
+                        f"sinks {s_}, window {w_}, top-k {k_} (budget {budget})",
+            "ms_per_call_median": round(ms, 4), "sparse_flop_per_call": flop,
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "whole call (ranks, cutoffs, lists, masked attention); flops count kept pairs only"}
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources: counter readings taken on other sources do not apply."""
     import hashlib
@@ -218,6 +255,10 @@ def main():
         out["config"]["workload"] += f" [profiling run: {L} layers only]"
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
+    if args.layers is None:
+        layers.clear()
+        torch.cuda.empty_cache()
+        out["budget_path"] = budget_measurement(kv, synth, dev)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
