@@ -105,6 +105,47 @@ def budget_measurement(kv, synth, dev, reps: int = 10):
             "note": "whole call (ranks, cutoffs, lists, masked attention); flops count kept pairs only"}
 
 
+def paper_pipeline_measurement(kv, q, k, v, window: int, reps: int = 5):
+    """Auxiliary (not part of `value`): the pages' training configuration of
+    the target on one layer of the metric workload: the budget-masked forward
+    (sinks 4, window w, top-k so that the budget is 2048, seeded N(0,1) static
+    scores) returns the sparse LSE, which feeds the transposed target pass
+    (Eq. 9 instead of the dense Eq. 8)."""
+    B_, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    sinks, topk = 4, 2048 - 4 - window
+    g = torch.Generator(device=q.device).manual_seed(2048)
+    scores = torch.randn(B_, Hkv, S, generator=g, device=q.device, dtype=torch.float32)
+    o = torch.empty_like(q)
+    lse = torch.empty(B_, Hq, S, dtype=torch.float32, device=q.device)
+    tgt = torch.empty(B_, Hkv, S, dtype=torch.float32, device=q.device)
+    wsb = torch.empty(kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=sinks, window=window, topk=topk),
+                      dtype=torch.uint8, device=q.device)
+    wst = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, q, k, window=window), dtype=torch.uint8,
+                      device=q.device)
+    stream = torch.cuda.current_stream(q.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms, tgt_ms = [], []
+    for i in range(reps + 2):
+        ev[0].record(stream)
+        kv.budget_mask_fwd(q, k, v, scores, sinks, window, topk, return_rank_cutoff=False, out=o, lse=lse,
+                           workspace=wsb, stream=stream)
+        ev[1].record(stream)
+        kv.future_target(q, k, lse, window, out=tgt, workspace=wst, stream=stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            fwd_ms.append(ev[0].elapsed_time(ev[1]))
+            tgt_ms.append(ev[1].elapsed_time(ev[2]))
+    fwd_ms.sort()
+    tgt_ms.sort()
+    f, t_ = fwd_ms[len(fwd_ms) // 2], tgt_ms[len(tgt_ms) // 2]
+    return {"workload": f"one layer of the metric workload (B={B_}, S={S}, {Hq}q/{Hkv}kv, D={D}), budget "
+                        f"{sinks}+{window}+{topk}=2048, seeded N(0,1) scores; sparse LSE -> target",
+            "budget_fwd_ms": round(f, 4), "target_ms": round(t_, 4), "layer_ms": round(f + t_, 4),
+            "keys_per_s": round(B_ * Hkv * S / ((f + t_) * 1e-3), 1)}
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources: counter readings taken on other sources do not apply."""
     import hashlib
@@ -256,6 +297,7 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
     if args.layers is None:
+        out["paper_pipeline"] = paper_pipeline_measurement(kv, layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
         layers.clear()
         torch.cuda.empty_cache()
         out["budget_path"] = budget_measurement(kv, synth, dev)

@@ -1,0 +1,82 @@
+"""GPU parity of the paper's training configuration of the target: the sparse
+normaliser L~ returned by the budget-masked forward (KVpop paper, Section 3.2,
+Eq. 9: the student's sparse LSE stands in for the dense causal one) fed into
+the transposed target pass.
+
+Reference: the oracle's masked attention gives L~, and the oracle's transposed
+formulation of Eq. 8 (original keys as queries, -L~_d as the score modifier,
+block mask d >= t + w) gives ln sum_{d >= t+w} exp(s_{d,t} - L~_d) per query
+head.  The GPU side chains its own kernels (budget forward -> target), so its
+L~ carries the forward's rounding; the target tolerance (2e-2) absorbs the
+LSE tolerance (2e-3).  Runs on an MI355X."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import budget, dense
+from tests.parity import assert_lse_close, assert_target_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def reference_target(q, k, scores, s, w, topk, heads):
+    q64, k64 = dense.to_f64(q), dense.to_f64(k)
+    r_rank, r_cut = budget.budget_reference(scores.cpu().numpy(), s, w, topk)
+    v64 = np.zeros_like(k64)  # the output is not needed here
+    _, lse_sparse = budget.masked_attention(q64, k64, v64, r_rank, r_cut, s, w, heads=heads)
+    tl = dense.transposed_lse(q64, k64, lse_sparse, window=w, heads=heads)
+    return lse_sparse, tl
+
+
+CASES = [
+    # S, Hq, Hkv, s, w, k, seed
+    (1500, 4, 1, 4, 64, 200, 1),
+    (2048, 8, 2, 4, 128, 300, 2),
+    (777, 4, 2, 0, 16, 50, 3),
+    (600, 4, 1, 8, 64, 1000, 4),   # budget larger than S: sparse = dense
+]
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,s,w,kk,seed", CASES)
+def test_target_with_sparse_lse(kvpop_lib, S, Hq, Hkv, s, w, kk, seed):
+    say(f"sparse-LSE target S={S} Hq={Hq} Hkv={Hkv} s={s} w={w} k={kk}")
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 500 + seed, device=DEV, heavy_hitters=True,
+                       with_scores=True)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    _, lse_sp, _, _ = kvpop_lib.budget_mask_fwd(q, k, v, sc, s, w, kk, return_rank_cutoff=False)
+    tg = kvpop_lib.future_target(q, k, lse_sp, w, agg="none")
+    tg_sum = kvpop_lib.future_target(q, k, lse_sp, w, agg="sum")
+    torch.cuda.synchronize()
+    heads = [(0, g) for g in range(Hq)]
+    r_lse, r_tl = reference_target(q, k, sc, s, w, kk, heads)
+    assert_lse_close(lse_sp, r_lse, what="sparse lse")
+    assert_target_close(tg, r_tl, what="target with sparse lse, per query head")
+    G = Hq // Hkv
+    with np.errstate(divide="ignore"):
+        r_sum = np.log(np.exp(r_tl).reshape(1, Hkv, G, S).sum(axis=2))
+    assert_target_close(tg_sum, r_sum, what="target with sparse lse, sum over the group")
+
+
+def test_sparse_lse_target_equals_dense_when_budget_covers_all(kvpop_lib):
+    """With s + w + k >= S the mask is full causal, so L~ = L: the sparse and
+    dense forwards give the same LSE (within the LSE tolerance, since the two
+    kernels sum the keys in different orders) and the same target."""
+    S, Hq, Hkv, w = 900, 4, 1, 32
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 77, device=DEV, with_scores=True)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    _, lse_sp, _, _ = kvpop_lib.budget_mask_fwd(q, k, v, sc, 4, w, S, return_rank_cutoff=False)
+    _, lse_dn = kvpop_lib.attn_fwd_lse(q, k, v, need_output=False)
+    t_sp = kvpop_lib.future_target(q, k, lse_sp, w)
+    t_dn = kvpop_lib.future_target(q, k, lse_dn, w)
+    torch.cuda.synchronize()
+    assert_lse_close(lse_sp, lse_dn.cpu().double().numpy(), what="sparse vs dense lse")
+    assert_target_close(t_sp, t_dn.cpu().double().numpy(), what="sparse-lse vs dense-lse target")

@@ -225,3 +225,34 @@ def test_invalid_cu_rejected():
         dense.doc_bounds(10, [0, 5, 5, 10])
     with pytest.raises(ValueError):
         dense.doc_bounds(10, [0, 5, 9])
+
+
+def test_transposed_lse_with_sparse_normaliser_matches_brute_force():
+    """The paper's training target (Eq. 9): the transposed formulation fed with
+    the budget-masked normaliser L~ equals the plain double sum
+    ln sum_{d >= t+w} exp(s_{d,t} - L~_d), evaluated term by term in pure
+    Python, on a tiny input.  L~ comes from an independent per-row loop over
+    the mask rows."""
+    import math
+    from oracle import budget
+    rng = np.random.default_rng(11)
+    S, D, s, w, kk = 23, 8, 2, 3, 4
+    q = rng.standard_normal((1, 1, S, D))
+    k = rng.standard_normal((1, 1, S, D))
+    scores = rng.standard_normal((1, 1, S))
+    rank, cut = budget.budget_reference(scores, s, w, kk)
+    M = budget.mask_rows(rank[0, 0], cut[0, 0], s, w, np.arange(S))
+    sc = 1.0 / math.sqrt(D)
+    Ls = np.empty(S)
+    for d in range(S):
+        terms = [sc * float(np.dot(q[0, 0, d], k[0, 0, t])) for t in range(S) if M[d, t]]
+        m = max(terms)
+        Ls[d] = m + math.log(math.fsum(math.exp(x - m) for x in terms))
+    got = dense.transposed_lse(q, k, Ls.reshape(1, 1, S), window=w)
+    for t in range(S):
+        terms = [sc * float(np.dot(q[0, 0, d], k[0, 0, t])) - Ls[d] for d in range(t + w, S)]
+        if not terms:
+            assert np.isneginf(got[0, 0, t])
+            continue
+        want = math.log(math.fsum(math.exp(x) for x in terms))
+        assert abs(got[0, 0, t] - want) < 1e-12
