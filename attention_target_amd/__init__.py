@@ -10,6 +10,8 @@ Entry points (same names as the C ABI, without the ``kvpop_`` prefix):
     attn_fwd_lse(q, k, v, ...)            -> (o, lse)
     future_target(q, k, lse, window, ...) -> target
     budget_mask_fwd(q, k, v, scores, sinks, window, topk, ...) -> (o, lse, rank, cutoff)
+    teacher_labels(target, sinks, window, topk, ...) -> (label, boundary)
+    boundary_loss(pred, label, boundary, sinks, window, topk, tau, ...) -> (loss, grad)
     workspace_size(which, ...)
 """
 from __future__ import annotations
@@ -30,7 +32,9 @@ CALL_FWD_LSE, CALL_FUTURE_TARGET, CALL_BUDGET_MASK_FWD = 0, 1, 2
 CUTOFF_ALL = 2 ** 31 - 1
 CUTOFF_NONE = -1
 EXPORTS = ("kvpop_attn_fwd_lse", "kvpop_future_target", "kvpop_budget_mask_fwd",
-           "kvpop_workspace_size", "kvpop_status_str", "kvpop_last_error")
+           "kvpop_workspace_size", "kvpop_status_str", "kvpop_last_error",
+           "kvpop_teacher_labels", "kvpop_teacher_workspace_size",
+           "kvpop_boundary_loss", "kvpop_boundary_loss_workspace_size")
 
 _AGG_NAMES = {"sum": AGG_SUM, "max": AGG_MAX, "none": AGG_NONE}
 
@@ -74,6 +78,14 @@ def load():
     lib.kvpop_status_str.restype = ctypes.c_char_p
     lib.kvpop_last_error.argtypes = []
     lib.kvpop_last_error.restype = ctypes.c_char_p
+    lib.kvpop_teacher_labels.argtypes = [I, I, I, P, P, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.kvpop_teacher_labels.restype = I
+    lib.kvpop_teacher_workspace_size.argtypes = [I, I, I]
+    lib.kvpop_teacher_workspace_size.restype = Z
+    lib.kvpop_boundary_loss.argtypes = [I, I, I, P, P, P, I, I, I, F, P, P, P, P, Z, P]
+    lib.kvpop_boundary_loss.restype = I
+    lib.kvpop_boundary_loss_workspace_size.argtypes = [I, I, I]
+    lib.kvpop_boundary_loss_workspace_size.restype = Z
     _lib = lib
     return lib
 
@@ -241,7 +253,65 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
     return out, lse, rank, cutoff
 
 
-__all__ = ["load", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+def teacher_labels(target: torch.Tensor, sinks: int, window: int, topk: int,
+                   decay_lambda: Optional[torch.Tensor] = None, decay_step: int = 1,
+                   return_ranks: bool = False, workspace: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None):
+    """Teacher labels at the eviction boundary (kvpop_teacher_labels).
+
+    target: [B, Hkv, S] fp32.  Returns (label, boundary) int32 [B, Hkv, S],
+    plus (rank, brank) when return_ranks."""
+    lib = load()
+    _require("target", target, torch.float32)
+    if target.dim() != 3:
+        raise ValueError("target must be [B, Hkv, S]")
+    B, H, S = target.shape
+    if decay_lambda is not None:
+        _require("decay_lambda", decay_lambda, torch.float32, (H,))
+    label = torch.empty(B, H, S, dtype=torch.int32, device=target.device)
+    bnd = torch.empty_like(label)
+    rank = brank = None
+    if return_ranks:
+        rank = torch.empty_like(label)
+        brank = torch.empty_like(label)
+    need = int(lib.kvpop_teacher_workspace_size(B, H, S))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=target.device)
+    _check(lib.kvpop_teacher_labels(B, H, S, target.data_ptr(), _dev(decay_lambda), int(decay_step), int(sinks),
+                                    int(window), int(topk), label.data_ptr(), bnd.data_ptr(), _dev(rank),
+                                    _dev(brank), workspace.data_ptr(), workspace.numel(),
+                                    _stream_ptr(target, stream)))
+    return (label, bnd, rank, brank) if return_ranks else (label, bnd)
+
+
+def boundary_loss(pred: torch.Tensor, label: torch.Tensor, boundary: torch.Tensor, sinks: int, window: int,
+                  topk: int, tau: float, weight: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Boundary-aware retention loss and its gradient (kvpop_boundary_loss).
+
+    Returns (loss per query position, d(sum loss)/d pred), both [B, Hkv, S] fp32."""
+    lib = load()
+    _require("pred", pred, torch.float32)
+    if pred.dim() != 3:
+        raise ValueError("pred must be [B, Hkv, S]")
+    B, H, S = pred.shape
+    _require("label", label, torch.int32, pred.shape)
+    _require("boundary", boundary, torch.int32, pred.shape)
+    if weight is not None:
+        _require("weight", weight, torch.float32, pred.shape)
+    loss = torch.empty_like(pred)
+    grad = torch.empty_like(pred)
+    need = int(lib.kvpop_boundary_loss_workspace_size(B, H, S))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pred.device)
+    _check(lib.kvpop_boundary_loss(B, H, S, pred.data_ptr(), label.data_ptr(), boundary.data_ptr(), int(sinks),
+                                   int(window), int(topk), float(tau), _dev(weight), loss.data_ptr(),
+                                   grad.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream_ptr(pred, stream)))
+    return loss, grad
+
+
+__all__ = ["load", "teacher_labels", "boundary_loss", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
            "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
            "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
            "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]

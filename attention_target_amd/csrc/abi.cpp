@@ -181,4 +181,63 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
                   "kvpop_budget_mask_fwd launch");
 }
 
+
+static kvpop_status check_seq(int32_t batch, int32_t n_kv_heads, int32_t seqlen) {
+  if (batch < 1 || n_kv_heads < 1 || seqlen < 1)
+    return fail(KVPOP_EINVAL, "batch, n_kv_heads and seqlen must be >= 1");
+  if (seqlen > (1 << 24)) return fail(KVPOP_EUNSUPPORTED, "seqlen %d exceeds 2^24", seqlen);
+  if ((double)batch * n_kv_heads * seqlen > 2.0e9) return fail(KVPOP_EUNSUPPORTED, "tensor too large");
+  return KVPOP_OK;
+}
+
+size_t kvpop_teacher_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t seqlen) {
+  if (check_seq(batch, n_kv_heads, seqlen) != KVPOP_OK) return 0;
+  return kvpop::teacher_workspace_bytes(batch, n_kv_heads, seqlen);
+}
+
+size_t kvpop_boundary_loss_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t seqlen) {
+  if (check_seq(batch, n_kv_heads, seqlen) != KVPOP_OK) return 0;
+  return kvpop::boundary_loss_workspace_bytes(batch, n_kv_heads, seqlen);
+}
+
+kvpop_status kvpop_teacher_labels(int32_t batch, int32_t n_kv_heads, int32_t seqlen, const float *target,
+                                  const float *decay_lambda, int32_t decay_step, int32_t sinks, int32_t window,
+                                  int32_t topk, int32_t *label, int32_t *boundary, int32_t *rank_out,
+                                  int32_t *brank_out, void *workspace, size_t ws_bytes, void *hip_stream) {
+  kvpop_status st = check_seq(batch, n_kv_heads, seqlen);
+  if (st != KVPOP_OK) return st;
+  if (!target || !label || !boundary) return fail(KVPOP_EINVAL, "target, label and boundary must be non-NULL");
+  if (sinks < 0 || window < 0 || topk < 0)
+    return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
+  if (decay_step < 1) return fail(KVPOP_EINVAL, "decay_step must be >= 1 (got %d)", decay_step);
+  const size_t need = kvpop::teacher_workspace_bytes(batch, n_kv_heads, seqlen);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_teacher(batch, n_kv_heads, seqlen, target, decay_lambda, decay_step, sinks, window,
+                                        topk, label, boundary, rank_out, brank_out, workspace,
+                                        (hipStream_t)hip_stream),
+                  "kvpop_teacher_labels launch");
+}
+
+kvpop_status kvpop_boundary_loss(int32_t batch, int32_t n_kv_heads, int32_t seqlen, const float *pred,
+                                 const int32_t *label, const int32_t *boundary, int32_t sinks, int32_t window,
+                                 int32_t topk, float tau, const float *weight, float *loss, float *grad,
+                                 void *workspace, size_t ws_bytes, void *hip_stream) {
+  kvpop_status st = check_seq(batch, n_kv_heads, seqlen);
+  if (st != KVPOP_OK) return st;
+  if (!pred || !label || !boundary || !loss || !grad)
+    return fail(KVPOP_EINVAL, "pred, label, boundary, loss and grad must be non-NULL");
+  if (sinks < 0 || window < 0 || topk < 0)
+    return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
+  if (!(tau > 0.f) || std::isinf(tau)) return fail(KVPOP_EINVAL, "tau must be finite and > 0");
+  const size_t need = kvpop::boundary_loss_workspace_bytes(batch, n_kv_heads, seqlen);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_boundary_loss(batch, n_kv_heads, seqlen, pred, label, boundary, sinks, window, topk,
+                                              tau, weight, loss, grad, workspace, (hipStream_t)hip_stream),
+                  "kvpop_boundary_loss launch");
+}
+
 }  // extern "C"

@@ -304,40 +304,42 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
   }
 }
 
+// k-th smallest (0-based kk) of the first m eligible ranks (positions
+// sinks .. sinks+m-1) on the wavelet matrix of (batch, KV head) bh.
+__device__ int wavelet_kth(const WaveletParams &p, size_t bh, int m, int kk) {
+  const int n_e = p.S - p.sinks;
+  int l = 0, r = m, val = 0;
+  for (int lvl = p.L - 1; lvl >= 0; --lvl) {
+    const uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+    const int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+    const int ol = pl[l >> 5] + __popc(bl[l >> 5] & ((1u << (l & 31)) - 1u));
+    const int orr = pl[r >> 5] + __popc(bl[r >> 5] & ((1u << (r & 31)) - 1u));
+    const int zin = (r - l) - (orr - ol);
+    if (kk < zin) {
+      l -= ol;
+      r -= orr;
+    } else {
+      kk -= zin;
+      const int Z = p.zeros[bh * p.L + lvl];
+      l = Z + ol;
+      r = Z + orr;
+      val |= 1 << lvl;
+    }
+    l = min(max(l, 0), n_e);  // stays in range for a well-formed matrix; guards the reads otherwise
+    r = min(max(r, l), n_e);
+  }
+  return val;
+}
+
 __global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int window, int topk, int *cutoff) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   const size_t bh = blockIdx.y;
   if (d >= p.S) return;
   const long long m_e = (long long)d - window - p.sinks + 1;  // |E_d|
   int res;
-  if (topk <= 0) {
-    res = CUT_NONE;
-  } else if (m_e < topk) {
-    res = CUT_ALL;
-  } else {
-    const int n_e = p.S - p.sinks;
-    int l = 0, r = (int)m_e, kk = topk - 1, val = 0;
-    for (int lvl = p.L - 1; lvl >= 0; --lvl) {
-      const uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
-      const int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
-      const int ol = pl[l >> 5] + __popc(bl[l >> 5] & ((1u << (l & 31)) - 1u));
-      const int orr = pl[r >> 5] + __popc(bl[r >> 5] & ((1u << (r & 31)) - 1u));
-      const int zin = (r - l) - (orr - ol);
-      if (kk < zin) {
-        l -= ol;
-        r -= orr;
-      } else {
-        kk -= zin;
-        const int Z = p.zeros[bh * p.L + lvl];
-        l = Z + ol;
-        r = Z + orr;
-        val |= 1 << lvl;
-      }
-      l = min(max(l, 0), n_e);  // stays in range for a well-formed matrix; guards the reads otherwise
-      r = min(max(r, l), n_e);
-    }
-    res = val;
-  }
+  if (topk <= 0) res = CUT_NONE;
+  else if (m_e < topk) res = CUT_ALL;
+  else res = wavelet_kth(p, bh, (int)m_e, topk - 1);
   cutoff[bh * p.S + d] = res;
 }
 
@@ -518,6 +520,237 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   if (s.dtype == 0 && s.D == 64) return run_sparse<bf16, 64>(fp, grid, st);
   if (s.dtype == 1 && s.D == 64) return run_sparse<float, 64>(fp, grid, st);
   return hipErrorInvalidValue;
+}
+
+// ===========================================================================
+// Teacher labels at the eviction boundary (KVpop paper, Section 3.1, Eqs.
+// 4-6) and the boundary-aware retention loss (Eq. 7).
+//
+// The teacher ranks the eligible tokens E_d = [s, d-w] by effective scores
+// (the target minus a per-head decay of lambda per Delta positions of age)
+// and keeps the top-k.  Section 3.2's running threshold over static
+// priorities applies: pi(t) = y(t) + (lambda/Delta)*t (the age term's
+// query-dependent part is shared by all eligible tokens; exact when
+// lambda = 0 or Delta = 1).  The rank/wavelet engine of the budget mask then
+// gives, for every d, the boundary rank b_d = the min(k, |E_d|)-th smallest
+// rank of E_d (the last kept token), the boundary token of that rank, and the
+// label of the newly eligible token d-w: rank(d-w) <= b_d.
+
+__global__ void __launch_bounds__(256) teacher_keys(const float *y, const float *lam, int delta, uint64_t *keys,
+                                                    int S, int S_pad, int Hkv) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= S_pad) return;
+  uint64_t key = ~0ull;
+  if (t < S) {
+    const float c = (lam != nullptr) ? __fdiv_rn(lam[bh % Hkv], (float)delta) : 0.f;
+    const float pri = __fadd_rn(y[bh * S + t], __fmul_rn(c, (float)t));  // no contraction: same rounding as the reference
+    key = score_key(pri, t);
+  }
+  keys[bh * S_pad + t] = key;
+}
+
+__global__ void __launch_bounds__(256) teacher_order(const int *rank, int *order, int S) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= S) return;
+  const int r = rank[bh * S + t];
+  if (r >= 0 && r < S) order[bh * S + r] = t;
+}
+
+struct TeacherParams {
+  WaveletParams wp;
+  const int *rank, *order;
+  int *label, *boundary, *brank;
+  int window, topk;
+};
+
+__global__ void __launch_bounds__(256) teacher_bounds(const TeacherParams p) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  const int S = p.wp.S;
+  if (d >= S) return;
+  const long long m_e = (long long)d - p.window - p.wp.sinks + 1;  // |E_d|
+  int lab = -1, bnd = -1, br = -1;
+  if (p.topk > 0 && m_e > 0) {
+    const int m = (int)m_e;
+    br = wavelet_kth(p.wp, bh, m, min(p.topk, m) - 1);
+    if (br >= 0 && br < S) bnd = p.order[bh * S + br];
+    lab = (p.rank[bh * S + d - p.window] <= br) ? 1 : 0;
+  }
+  p.label[bh * S + d] = lab;
+  p.boundary[bh * S + d] = bnd;
+  if (p.brank != nullptr) p.brank[bh * S + d] = br;
+}
+
+struct TeacherLayout {
+  size_t keys, sorted, rank, order, arr0, arr1, bits, prefix, zeros, total;
+  int S_pad, nchunks, L, nw1;
+};
+
+static TeacherLayout teacher_layout(int B, int Hkv, int S) {
+  TeacherLayout lo{};
+  const size_t BH = (size_t)B * Hkv;
+  lo.nchunks = (S + RANK_CH - 1) / RANK_CH;
+  lo.S_pad = lo.nchunks * RANK_CH;
+  lo.L = 1;
+  while ((1ll << lo.L) < (long long)S) ++lo.L;
+  lo.nw1 = (S + 31) / 32 + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = al256(off + bytes);
+    return o;
+  };
+  lo.keys = take(BH * lo.S_pad * 8);
+  lo.sorted = take(BH * lo.S_pad * 8);
+  lo.rank = take(BH * S * 4);
+  lo.order = take(BH * S * 4);
+  lo.arr0 = take(BH * S * 4);
+  lo.arr1 = take(BH * S * 4);
+  lo.bits = take(BH * lo.L * lo.nw1 * 4);
+  lo.prefix = take(BH * lo.L * lo.nw1 * 4);
+  lo.zeros = take(BH * lo.L * 4);
+  lo.total = off;
+  return lo;
+}
+
+size_t teacher_workspace_bytes(int B, int Hkv, int S) { return teacher_layout(B, Hkv, S).total; }
+
+hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *lam, int delta, int sinks, int window,
+                          int topk, int *label, int *boundary, int *rank_out, int *brank_out, void *ws,
+                          hipStream_t st) {
+  const TeacherLayout lo = teacher_layout(B, Hkv, S);
+  char *w = reinterpret_cast<char *>(ws);
+  const int BH = B * Hkv;
+  uint64_t *keys = reinterpret_cast<uint64_t *>(w + lo.keys);
+  uint64_t *sorted = reinterpret_cast<uint64_t *>(w + lo.sorted);
+  int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
+  int *order = reinterpret_cast<int *>(w + lo.order);
+  hipLaunchKernelGGL(teacher_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, y, lam, delta, keys, S, lo.S_pad, Hkv);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(256), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_rank, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, S, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(teacher_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TeacherParams tp{};
+  WaveletParams &wp = tp.wp;
+  wp.rank = rank;
+  wp.arr0 = reinterpret_cast<int *>(w + lo.arr0);
+  wp.arr1 = reinterpret_cast<int *>(w + lo.arr1);
+  wp.bits = reinterpret_cast<uint32_t *>(w + lo.bits);
+  wp.prefix = reinterpret_cast<int *>(w + lo.prefix);
+  wp.zeros = reinterpret_cast<int *>(w + lo.zeros);
+  wp.S = S;
+  wp.sinks = sinks;
+  wp.L = lo.L;
+  wp.nw1 = lo.nw1;
+  if (topk > 0 && S - sinks > 0) {
+    if (S - sinks <= WV_LDS_MAX && S <= 65536 && lo.nw1 <= WV_LDS_WORDS)
+      hipLaunchKernelGGL(budget_wavelet_build_lds, dim3(BH), dim3(1024), 0, st, wp);
+    else
+      hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
+  }
+  tp.rank = rank;
+  tp.order = order;
+  tp.label = label;
+  tp.boundary = boundary;
+  tp.brank = brank_out;
+  tp.window = window;
+  tp.topk = topk;
+  hipLaunchKernelGGL(teacher_bounds, dim3((S + 255) / 256, BH), dim3(256), 0, st, tp);
+  return hipGetLastError();
+}
+
+// ---- Eq. 7: loss per query position and the gradient of the sum ----
+// loss_d = omega_d * softplus(-sign_d * x_d), x_d = (r(d-w) - r(t_bnd(d)))/tau.
+// Token d-w receives +g_d and the boundary token -g_d, g_d = dloss_d/dx_d /
+// tau.  Many d share one boundary token; since the boundary rank rises while
+// |E_d| < k and then falls (c_d is non-increasing), the d's of one boundary
+// token form at most one run before d* = s+w+k-1 and one from d* on.  Each
+// run is summed in d order by the thread of its first d and stored in that
+// phase's slot of the token, so the reduction is deterministic and needs no
+// atomics.
+
+struct LossParams {
+  const float *pred, *weight;
+  const int *label, *boundary;
+  float *loss, *grad, *gterm, *slot0, *slot1;
+  int S, window, dstar;
+  float inv_tau;
+};
+
+__global__ void __launch_bounds__(256) boundary_loss_terms(const LossParams p) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (d >= p.S) return;
+  const size_t i = bh * p.S + d;
+  const int lab = p.label[i], b = p.boundary[i], a = d - p.window;
+  float loss = 0.f, g = 0.f;
+  if (lab >= 0 && b >= 0 && b < p.S && a >= 0) {
+    const float sgn = lab == 1 ? 1.f : -1.f;
+    const float om = p.weight ? p.weight[i] : 1.f;
+    const float x = (p.pred[bh * p.S + a] - p.pred[bh * p.S + b]) * p.inv_tau;
+    const float z = -sgn * x;
+    loss = om * (fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))));
+    const float sig = expf(fminf(z, 0.f)) / (1.f + expf(-fabsf(z)));
+    g = -sgn * om * sig * p.inv_tau;
+  }
+  p.loss[i] = loss;
+  p.gterm[i] = g;
+  p.slot0[i] = 0.f;
+  p.slot1[i] = 0.f;
+}
+
+__global__ void __launch_bounds__(256) boundary_loss_runs(const LossParams p) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (d >= p.S) return;
+  const int *bd = p.boundary + bh * p.S;
+  const int b = bd[d];
+  if (b < 0 || b >= p.S || (d > 0 && bd[d - 1] == b)) return;  // not the first d of a run
+  float sum = 0.f;
+  for (int e = d; e < p.S && bd[e] == b; ++e) sum += p.gterm[bh * p.S + e];
+  float *slot = (d < p.dstar) ? p.slot0 : p.slot1;
+  slot[bh * p.S + b] = sum;
+}
+
+__global__ void __launch_bounds__(256) boundary_loss_grad(const LossParams p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= p.S) return;
+  const size_t i = bh * p.S + t;
+  const float g_new = (t + p.window < p.S) ? p.gterm[i + p.window] : 0.f;
+  p.grad[i] = g_new - p.slot0[i] - p.slot1[i];
+}
+
+size_t boundary_loss_workspace_bytes(int B, int Hkv, int S) { return 3 * al256((size_t)B * Hkv * S * 4); }
+
+hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const int *label, const int *boundary,
+                                int sinks, int window, int topk, float tau, const float *weight, float *loss,
+                                float *grad, void *ws, hipStream_t st) {
+  LossParams lp{};
+  const size_t n = al256((size_t)B * Hkv * S * 4);
+  char *w = reinterpret_cast<char *>(ws);
+  lp.pred = pred;
+  lp.weight = weight;
+  lp.label = label;
+  lp.boundary = boundary;
+  lp.loss = loss;
+  lp.grad = grad;
+  lp.gterm = reinterpret_cast<float *>(w);
+  lp.slot0 = reinterpret_cast<float *>(w + n);
+  lp.slot1 = reinterpret_cast<float *>(w + 2 * n);
+  lp.S = S;
+  lp.window = window;
+  const long long ds = (long long)sinks + window + topk - 1;
+  lp.dstar = (int)min(max(ds, 0ll), (long long)S);
+  lp.inv_tau = 1.f / tau;
+  const dim3 grid((S + 255) / 256, B * Hkv);
+  hipLaunchKernelGGL(boundary_loss_terms, grid, dim3(256), 0, st, lp);
+  hipLaunchKernelGGL(boundary_loss_runs, grid, dim3(256), 0, st, lp);
+  hipLaunchKernelGGL(boundary_loss_grad, grid, dim3(256), 0, st, lp);
+  return hipGetLastError();
 }
 
 }  // namespace kvpop

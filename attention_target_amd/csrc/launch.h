@@ -29,6 +29,15 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
                          const float *scores, int sinks, int window, int topk, void *o, float *lse,
                          int *rank_out, int *cutoff_out, void *ws, hipStream_t st);
 
+size_t teacher_workspace_bytes(int B, int Hkv, int S);
+hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *lam, int delta, int sinks, int window,
+                          int topk, int *label, int *boundary, int *rank_out, int *brank_out, void *ws,
+                          hipStream_t st);
+size_t boundary_loss_workspace_bytes(int B, int Hkv, int S);
+hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const int *label, const int *boundary,
+                                int sinks, int window, int topk, float tau, const float *weight, float *loss,
+                                float *grad, void *ws, hipStream_t st);
+
 // Query heads of one GQA group handled by one forward workgroup.
 inline int fwd_heads_per_block(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 

@@ -163,6 +163,60 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
 size_t kvpop_workspace_size(int32_t which, const kvpop_shape *shape, int32_t sinks,
                             int32_t window, int32_t topk);
 
+/*
+ * Teacher labels at the eviction boundary (Section 3.1, Eqs. 4-6).  For each
+ * (batch row, KV head) the teacher ranks the eligible tokens
+ * E_d = [sinks, d - window] by effective scores, the target y(t) minus a
+ * per-head decay of lambda per decay_step positions of age (Eq. 5), and
+ * keeps the top `topk`.  Section 3.2's running threshold over static
+ * priorities is used: pi(t) = y(t) + (lambda / decay_step) * t, computed in
+ * fp32 as c = lambda / decay_step, then y + c * t, each operation rounded
+ * (exact for lambda = 0 or decay_step = 1; otherwise the pages' own
+ * approximation up to the decay-step discretization).  Order: priority
+ * descending, ties (and -0.0 vs +0.0) to the lower index, NaN as -inf.
+ *
+ *  target [B,Hkv,S] fp32            y, e.g. kvpop_future_target's output (AGG_MAX, mean)
+ *  decay_lambda [Hkv] fp32          per-head decay, or NULL for none
+ *  decay_step >= 1, sinks, window, topk >= 0
+ *  label [B,Hkv,S] int32            label[d] = 1 if the teacher keeps the newly eligible
+ *                                   token d - window at query d, 0 if not, -1 when
+ *                                   d - window < sinks or topk == 0
+ *  boundary [B,Hkv,S] int32         the last kept token at query d (-1 if none): the token
+ *                                   of rank b_d = the min(topk, |E_d|)-th smallest rank of E_d
+ *  rank_out [B,Hkv,S] int32         optional (NULL): rank(t) under the priorities
+ *  brank_out [B,Hkv,S] int32        optional (NULL): b_d (-1 if none)
+ *  workspace, ws_bytes              >= kvpop_teacher_workspace_size()
+ */
+kvpop_status kvpop_teacher_labels(int32_t batch, int32_t n_kv_heads, int32_t seqlen, const float *target,
+                                  const float *decay_lambda, int32_t decay_step, int32_t sinks, int32_t window,
+                                  int32_t topk, int32_t *label, int32_t *boundary, int32_t *rank_out,
+                                  int32_t *brank_out, void *workspace, size_t ws_bytes, void *hip_stream);
+size_t kvpop_teacher_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t seqlen);
+
+/*
+ * Boundary-aware retention loss (Section 3.1, Eq. 7) and its gradient.  For
+ * every query position d with a label and a boundary token b = boundary[d]:
+ *   x_d = (pred[d - window] - pred[b]) / tau,  sign_d = +1 (kept) or -1,
+ *   loss[d] = weight[d] * ln(1 + exp(-sign_d * x_d))     (0 elsewhere)
+ * and grad = d(sum_d loss[d]) / d pred, per token.  The decay term is shared
+ * by the two tokens compared at one d, so raw predicted scores are compared.
+ *
+ *  pred [B,Hkv,S] fp32              raw predicted scores
+ *  label, boundary [B,Hkv,S] int32  from kvpop_teacher_labels with the same sinks, window
+ *                                   and topk (the deterministic gradient reduction relies
+ *                                   on their structure: the positions sharing a boundary
+ *                                   token form at most one run before d = sinks + window +
+ *                                   topk - 1 and one from there on)
+ *  tau > 0; weight [B,Hkv,S] fp32 per query position, or NULL for 1
+ *  loss, grad [B,Hkv,S] fp32        outputs
+ *  workspace, ws_bytes              >= kvpop_boundary_loss_workspace_size()
+ */
+kvpop_status kvpop_boundary_loss(int32_t batch, int32_t n_kv_heads, int32_t seqlen, const float *pred,
+                                 const int32_t *label, const int32_t *boundary, int32_t sinks, int32_t window,
+                                 int32_t topk, float tau, const float *weight, float *loss, float *grad,
+                                 void *workspace, size_t ws_bytes, void *hip_stream);
+size_t kvpop_boundary_loss_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t seqlen);
+
 /* Static description of a status code. */
 const char *kvpop_status_str(kvpop_status status);
 

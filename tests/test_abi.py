@@ -147,3 +147,29 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kv.attn_fwd_lse(q, q[:, :1], q[:, :1])
+
+
+def test_teacher_and_loss_validation():
+    lib = kv.load()
+    P = ctypes.c_void_p
+    dummy = ctypes.c_void_p(16)
+    # bad sizes, null pointers, negative parameters, decay step, tau
+    assert lib.kvpop_teacher_labels(0, 1, 10, dummy, None, 1, 0, 0, 1, dummy, dummy, None, None, dummy, 1 << 20,
+                                    None) == kv.EINVAL
+    assert lib.kvpop_teacher_labels(1, 1, 10, None, None, 1, 0, 0, 1, dummy, dummy, None, None, dummy, 1 << 20,
+                                    None) == kv.EINVAL
+    assert lib.kvpop_teacher_labels(1, 1, 10, dummy, None, 0, 0, 0, 1, dummy, dummy, None, None, dummy, 1 << 20,
+                                    None) == kv.EINVAL
+    assert lib.kvpop_teacher_labels(1, 1, 10, dummy, None, 1, -1, 0, 1, dummy, dummy, None, None, dummy, 1 << 20,
+                                    None) == kv.EINVAL
+    assert lib.kvpop_teacher_labels(1, 1, 10, dummy, None, 1, 0, 0, 1, dummy, dummy, None, None, dummy, 1,
+                                    None) == kv.EWORKSPACE
+    assert lib.kvpop_boundary_loss(1, 1, 10, dummy, dummy, dummy, 0, 0, 1, 0.0, None, dummy, dummy, dummy, 1 << 20,
+                                   None) == kv.EINVAL
+    assert lib.kvpop_boundary_loss(1, 1, 10, dummy, None, dummy, 0, 0, 1, 1.0, None, dummy, dummy, dummy, 1 << 20,
+                                   None) == kv.EINVAL
+    assert lib.kvpop_boundary_loss(1, 1, 10, dummy, dummy, dummy, 0, 0, 1, 1.0, None, dummy, dummy, dummy, 1,
+                                   None) == kv.EWORKSPACE
+    assert lib.kvpop_teacher_workspace_size(1, 2, 1000) > 0
+    assert lib.kvpop_teacher_workspace_size(0, 2, 1000) == 0
+    assert lib.kvpop_boundary_loss_workspace_size(2, 2, 1000) >= 3 * 2 * 2 * 1000 * 4
