@@ -146,6 +146,39 @@ def paper_pipeline_measurement(kv, q, k, v, window: int, reps: int = 5):
             "keys_per_s": round(B_ * Hkv * S / ((f + t_) * 1e-3), 1)}
 
 
+def teacher_measurement(kv, tgt, window: int, reps: int = 10):
+    """Auxiliary (not part of `value`): teacher labels at the eviction
+    boundary and the boundary loss with its gradient, on the target of one
+    layer of the metric workload ([B, Hkv, S] = [2, 8, 16384]), budget
+    4 + window + top-k = 2048, per-head decay 0.01 every 16 positions."""
+    B_, H, S = tgt.shape
+    sinks, topk = 4, 2048 - 4 - window
+    lam = torch.full((H,), 0.01, dtype=torch.float32, device=tgt.device)
+    g = torch.Generator(device=tgt.device).manual_seed(7)
+    pred = torch.randn(B_, H, S, generator=g, device=tgt.device, dtype=torch.float32)
+    y = torch.where(torch.isfinite(tgt), tgt, torch.full_like(tgt, -30.0)).contiguous()
+    stream = torch.cuda.current_stream(tgt.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_ms, l_ms = [], []
+    for i in range(reps + 2):
+        ev[0].record(stream)
+        lab, bnd = kv.teacher_labels(y, sinks, window, topk, decay_lambda=lam, decay_step=16, stream=stream)
+        ev[1].record(stream)
+        kv.boundary_loss(pred, lab, bnd, sinks, window, topk, 1.0, stream=stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            t_ms.append(ev[0].elapsed_time(ev[1]))
+            l_ms.append(ev[1].elapsed_time(ev[2]))
+    t_ms.sort()
+    l_ms.sort()
+    return {"workload": f"target of one layer of the metric workload [{B_}, {H}, {S}], budget {sinks}+{window}+"
+                        f"{topk}=2048, decay 0.01 per 16 positions",
+            "teacher_labels_ms": round(t_ms[len(t_ms) // 2], 4),
+            "boundary_loss_ms": round(l_ms[len(l_ms) // 2], 4),
+            "note": "each call includes its workspace allocation by the binding"}
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources: counter readings taken on other sources do not apply."""
     import hashlib
@@ -298,6 +331,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
     if args.layers is None:
         out["paper_pipeline"] = paper_pipeline_measurement(kv, layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
+        out["teacher_and_loss"] = teacher_measurement(kv, layers[0]["tgt"], w)
         layers.clear()
         torch.cuda.empty_cache()
         out["budget_path"] = budget_measurement(kv, synth, dev)
