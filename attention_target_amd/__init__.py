@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, without the ``kvpop_`` prefix):
     budget_mask_fwd(q, k, v, scores, sinks, window, topk, ...) -> (o, lse, rank, cutoff)
     teacher_labels(target, sinks, window, topk, ...) -> (label, boundary)
     boundary_loss(pred, label, boundary, sinks, window, topk, tau, ...) -> (loss, grad)
+    DecodeCache(...).step(q, k, v, score) -> (o, lse)   (decode_state_size / decode_init / decode_step)
     workspace_size(which, ...)
 """
 from __future__ import annotations
@@ -34,7 +35,8 @@ CUTOFF_NONE = -1
 EXPORTS = ("kvpop_attn_fwd_lse", "kvpop_future_target", "kvpop_budget_mask_fwd",
            "kvpop_workspace_size", "kvpop_status_str", "kvpop_last_error",
            "kvpop_teacher_labels", "kvpop_teacher_workspace_size",
-           "kvpop_boundary_loss", "kvpop_boundary_loss_workspace_size")
+           "kvpop_boundary_loss", "kvpop_boundary_loss_workspace_size",
+           "kvpop_decode_state_size", "kvpop_decode_init", "kvpop_decode_step")
 
 _AGG_NAMES = {"sum": AGG_SUM, "max": AGG_MAX, "none": AGG_NONE}
 
@@ -45,6 +47,12 @@ class Shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("cu_seqlens", ctypes.c_void_p),
                 ("cu_seqlens_host", ctypes.c_void_p), ("n_docs", ctypes.c_int32)]
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("sinks", ctypes.c_int32), ("window", ctypes.c_int32), ("topk", ctypes.c_int32)]
 
 
 class KvpopError(RuntimeError):
@@ -86,6 +94,13 @@ def load():
     lib.kvpop_boundary_loss.restype = I
     lib.kvpop_boundary_loss_workspace_size.argtypes = [I, I, I]
     lib.kvpop_boundary_loss_workspace_size.restype = Z
+    DP = ctypes.POINTER(DecodeShape)
+    lib.kvpop_decode_state_size.argtypes = [DP]
+    lib.kvpop_decode_state_size.restype = Z
+    lib.kvpop_decode_init.argtypes = [DP, P, Z, P]
+    lib.kvpop_decode_init.restype = I
+    lib.kvpop_decode_step.argtypes = [DP, P, Z, I, P, P, P, P, P, P, P]
+    lib.kvpop_decode_step.restype = I
     _lib = lib
     return lib
 
@@ -311,7 +326,51 @@ def boundary_loss(pred: torch.Tensor, label: torch.Tensor, boundary: torch.Tenso
     return loss, grad
 
 
-__all__ = ["load", "teacher_labels", "boundary_loss", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+class DecodeCache:
+    """Fixed-budget decode cache (kvpop_decode_init / kvpop_decode_step).
+
+    Holds the caller-owned state tensor; step() appends the next token and
+    returns the attention output and LSE of its query over the retained
+    slots."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 sinks: int, window: int, topk: int, scale: float = 0.0, device="cuda",
+                 stream: Optional[torch.cuda.Stream] = None):
+        lib = load()
+        self.shape = DecodeShape(batch, n_q_heads, n_kv_heads, head_dim,
+                                 BF16 if dtype == torch.bfloat16 else F32, float(scale), sinks, window, topk)
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("dtype must be bfloat16 or float32")
+        self.dtype = dtype
+        need = int(lib.kvpop_decode_state_size(ctypes.byref(self.shape)))
+        if need == 0:
+            raise KvpopError(EINVAL, f"kvpop: invalid decode shape: {last_error()}")
+        self.state = torch.empty(need, dtype=torch.uint8, device=device)
+        self.position = 0
+        s = stream if stream is not None else torch.cuda.current_stream(self.state.device)
+        _check(lib.kvpop_decode_init(ctypes.byref(self.shape), self.state.data_ptr(), self.state.numel(),
+                                     s.cuda_stream))
+
+    def step(self, q, k, v, score, out=None, lse=None, stream: Optional[torch.cuda.Stream] = None):
+        """q [B,Hq,D], k, v [B,Hkv,D] (the cache dtype), score [B,Hkv] fp32."""
+        lib = load()
+        sh = self.shape
+        _require("q", q, self.dtype, (sh.batch, sh.n_q_heads, sh.head_dim))
+        _require("k", k, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
+        _require("v", v, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
+        _require("score", score, torch.float32, (sh.batch, sh.n_kv_heads))
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(sh.batch, sh.n_q_heads, dtype=torch.float32, device=q.device)
+        _check(lib.kvpop_decode_step(ctypes.byref(sh), self.state.data_ptr(), self.state.numel(), self.position,
+                                     q.data_ptr(), k.data_ptr(), v.data_ptr(), score.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), _stream_ptr(q, stream)))
+        self.position += 1
+        return out, lse
+
+
+__all__ = ["load", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
            "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
            "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
            "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]

@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvpop.so")
 ARCH = "gfx950"
 
-SOURCES = ["fwd_lse.hip", "future_target.hip", "budget.hip", "abi.cpp"]
+SOURCES = ["fwd_lse.hip", "future_target.hip", "budget.hip", "decode.hip", "abi.cpp"]
 
 
 def hipcc() -> str:

@@ -240,4 +240,67 @@ kvpop_status kvpop_boundary_loss(int32_t batch, int32_t n_kv_heads, int32_t seql
                   "kvpop_boundary_loss launch");
 }
 
+
+static kvpop_status check_decode_shape(const kvpop_decode_shape *sh, kvpop::DecodeShapeInfo &s) {
+  if (sh == nullptr) return fail(KVPOP_EINVAL, "shape is NULL");
+  if (sh->batch < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1)
+    return fail(KVPOP_EINVAL, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (sh->n_q_heads % sh->n_kv_heads != 0)
+    return fail(KVPOP_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", sh->n_q_heads, sh->n_kv_heads);
+  if (sh->n_q_heads / sh->n_kv_heads > 8)
+    return fail(KVPOP_EUNSUPPORTED, "decoding supports at most 8 query heads per KV head");
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(KVPOP_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", sh->head_dim);
+  if (sh->dtype != KVPOP_BF16 && sh->dtype != KVPOP_F32)
+    return fail(KVPOP_EUNSUPPORTED, "dtype %d is not supported", sh->dtype);
+  if (sh->sinks < 0 || sh->window < 0 || sh->topk < 0)
+    return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0");
+  const long long C = (long long)sh->sinks + sh->window + sh->topk;
+  if (C < 1) return fail(KVPOP_EINVAL, "the cache needs at least one slot (sinks + window + topk >= 1)");
+  if (C > (1 << 20)) return fail(KVPOP_EUNSUPPORTED, "cache of %lld slots exceeds 2^20", C);
+  s.B = sh->batch;
+  s.Hq = sh->n_q_heads;
+  s.Hkv = sh->n_kv_heads;
+  s.D = sh->head_dim;
+  s.dtype = sh->dtype;
+  s.scale = (sh->softmax_scale > 0.f) ? sh->softmax_scale : (float)(1.0 / std::sqrt((double)sh->head_dim));
+  s.sinks = sh->sinks;
+  s.window = sh->window;
+  s.topk = sh->topk;
+  s.C = (int)C;
+  return KVPOP_OK;
+}
+
+size_t kvpop_decode_state_size(const kvpop_decode_shape *shape) {
+  kvpop::DecodeShapeInfo s{};
+  if (check_decode_shape(shape, s) != KVPOP_OK) return 0;
+  return kvpop::decode_state_bytes(s);
+}
+
+kvpop_status kvpop_decode_init(const kvpop_decode_shape *shape, void *state, size_t state_bytes, void *hip_stream) {
+  kvpop::DecodeShapeInfo s{};
+  kvpop_status st = check_decode_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (state == nullptr || state_bytes < kvpop::decode_state_bytes(s))
+    return fail(KVPOP_EWORKSPACE, "decode state of %zu bytes needed", kvpop::decode_state_bytes(s));
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_decode_init(s, state, (hipStream_t)hip_stream), "kvpop_decode_init launch");
+}
+
+kvpop_status kvpop_decode_step(const kvpop_decode_shape *shape, void *state, size_t state_bytes, int32_t position,
+                               const void *q, const void *k, const void *v, const float *score, void *o, float *lse,
+                               void *hip_stream) {
+  kvpop::DecodeShapeInfo s{};
+  kvpop_status st = check_decode_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !v || !score || !o || !lse)
+    return fail(KVPOP_EINVAL, "q, k, v, score, o and lse must be non-NULL");
+  if (position < 0) return fail(KVPOP_EINVAL, "position must be >= 0 (got %d)", position);
+  if (state == nullptr || state_bytes < kvpop::decode_state_bytes(s))
+    return fail(KVPOP_EWORKSPACE, "decode state of %zu bytes needed", kvpop::decode_state_bytes(s));
+  if ((st = check_device()) != KVPOP_OK) return st;
+  return from_hip(kvpop::launch_decode_step(s, state, position, q, k, v, score, o, lse, (hipStream_t)hip_stream),
+                  "kvpop_decode_step launch");
+}
+
 }  // extern "C"

@@ -38,6 +38,17 @@ hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const 
                                 int sinks, int window, int topk, float tau, const float *weight, float *loss,
                                 float *grad, void *ws, hipStream_t st);
 
+// Fixed-budget decoding (see kvpop_decode_shape in include/kvpop.h).
+struct DecodeShapeInfo {
+  int B, Hq, Hkv, D, dtype;
+  float scale;
+  int sinks, window, topk, C;  // C = sinks + window + topk slots
+};
+size_t decode_state_bytes(const DecodeShapeInfo &s);
+hipError_t launch_decode_init(const DecodeShapeInfo &s, void *state, hipStream_t st);
+hipError_t launch_decode_step(const DecodeShapeInfo &s, void *state, int position, const void *q, const void *k,
+                              const void *v, const float *score, void *o, float *lse, hipStream_t st);
+
 // Query heads of one GQA group handled by one forward workgroup.
 inline int fwd_heads_per_block(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 

@@ -217,6 +217,38 @@ kvpop_status kvpop_boundary_loss(int32_t batch, int32_t n_kv_heads, int32_t seql
                                  void *workspace, size_t ws_bytes, void *hip_stream);
 size_t kvpop_boundary_loss_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t seqlen);
 
+/*
+ * Fixed-budget decoding (Section 3: sinks, protected window and top-k;
+ * Section 3.2, "Running top-k sparse attention"; Section 4.3 measures the
+ * resulting bounded cache).  The state holds, per (batch row, KV head),
+ * sinks + window + topk slots of K and V plus bookkeeping; it is
+ * caller-owned device memory of kvpop_decode_state_size() bytes, set up by
+ * kvpop_decode_init().  kvpop_decode_step() appends token `position` (which
+ * must be 0, 1, 2, ... in order after init; the state does not check it):
+ * token position - window leaves the window and competes for the top-k by
+ * its static priority (score descending, ties to the lower index); if the
+ * top-k is full and it beats the worst retained token, that token is
+ * evicted for good.  The query of the new token then attends over the
+ * retained slots, which are exactly the budget mask's row `position` of
+ * kvpop_budget_mask_fwd with the same scores.
+ *
+ *  q [B,Hq,D], k, v [B,Hkv,D]   the new token (dtype)
+ *  score [B,Hkv] fp32           its static priority
+ *  o [B,Hq,D] (dtype), lse [B,Hq] fp32   outputs
+ * At most 8 query heads per KV head; head_dim 64 or 128.
+ */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t dtype;        /* KVPOP_BF16 or KVPOP_F32 */
+  float softmax_scale;  /* <= 0: 1/sqrt(head_dim) */
+  int32_t sinks, window, topk;
+} kvpop_decode_shape;
+size_t kvpop_decode_state_size(const kvpop_decode_shape *shape);
+kvpop_status kvpop_decode_init(const kvpop_decode_shape *shape, void *state, size_t state_bytes, void *hip_stream);
+kvpop_status kvpop_decode_step(const kvpop_decode_shape *shape, void *state, size_t state_bytes, int32_t position,
+                               const void *q, const void *k, const void *v, const float *score, void *o,
+                               float *lse, void *hip_stream);
+
 /* Static description of a status code. */
 const char *kvpop_status_str(kvpop_status status);
 
