@@ -179,6 +179,39 @@ def teacher_measurement(kv, tgt, window: int, reps: int = 10):
             "note": "each call includes its workspace allocation by the binding"}
 
 
+def decode_measurement(kv, dev, steps_fill: int = 2560, steps_timed: int = 200):
+    """Auxiliary (not part of `value`): fixed-budget decoding of one layer of
+    the pages' inference workload shape (batch 1, 32 query / 8 KV heads,
+    head_dim 128, bf16), budget 4 + 128 + 1916 = 2048, at steady state (the
+    cache full and evicting), timed per step with HIP events."""
+    B_, Hq, Hkv, D = 1, 32, 8, 128
+    sinks, window, topk = 4, 128, 1916
+    n = steps_fill + steps_timed
+    g = torch.Generator(device=dev).manual_seed(4096)
+    q = torch.randn(n, B_, Hq, D, generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn(n, B_, Hkv, D, generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn(n, B_, Hkv, D, generator=g, device=dev).to(torch.bfloat16)
+    sc = torch.randn(n, B_, Hkv, generator=g, device=dev, dtype=torch.float32)
+    cache = kv.DecodeCache(B_, Hq, Hkv, D, torch.bfloat16, sinks, window, topk, device=dev)
+    o = torch.empty(B_, Hq, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B_, Hq, dtype=torch.float32, device=dev)
+    for i in range(steps_fill):
+        cache.step(q[i], k[i], v[i], sc[i], out=o, lse=lse)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps_fill, n):
+        cache.step(q[i], k[i], v[i], sc[i], out=o, lse=lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps_timed
+    return {"workload": f"one layer, batch {B_}, {Hq}q/{Hkv}kv, D={D}, bf16, budget {sinks}+{window}+{topk}=2048, "
+                        f"steady state after {steps_fill} tokens",
+            "us_per_step": round(us, 2), "state_bytes_per_layer": int(cache.state.numel()),
+            "note": "update + attention + combine launches; the state size does not grow with the sequence"}
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources: counter readings taken on other sources do not apply."""
     import hashlib
@@ -335,6 +368,7 @@ def main():
         layers.clear()
         torch.cuda.empty_cache()
         out["budget_path"] = budget_measurement(kv, synth, dev)
+        out["decode"] = decode_measurement(kv, dev)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
