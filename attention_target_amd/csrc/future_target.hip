@@ -40,7 +40,11 @@
 
 namespace kvpop {
 
-constexpr int TGT_KT = 256;  // keys per block: 4 waves x 64
+#ifndef KVPOP_TGT_NCB
+#define KVPOP_TGT_NCB 2
+#endif
+constexpr int TGT_NCB = KVPOP_TGT_NCB;   // 32-key column blocks per wave
+constexpr int TGT_KT = 4 * 32 * TGT_NCB;  // keys per block: 4 waves
 
 struct TgtParams {
   const void *q, *k;
@@ -120,7 +124,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  const int tw = t0 + 64 * wave;  // doc-local first key of this wave
+  constexpr int NCB = TGT_NCB;
+  const int tw = t0 + 32 * NCB * wave;  // doc-local first key of this wave
   const int w = p.window;
 
   // ---- resident K fragments (B operand), pre-multiplied by scale*log2(e) ----
@@ -129,9 +134,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
   // holding scale*log2(e) and the MFMA addend holding -L_d*log2(e), the
   // accumulator is already the exp2 argument s_{d,t}*log2(e) - L_d*log2(e).
   const T *kbase = reinterpret_cast<const T *>(p.k) + ((size_t)b * p.Hkv + h) * (size_t)p.S * D;
-  Frag<T> kf[2][NJ];
+  Frag<T> kf[NCB][NJ];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const int key = min(tw + 32 * cb + col, n - 1);
     const T *kr = kbase + (size_t)(dstart + key) * D + 8 * hf;
 #pragma unroll
@@ -148,7 +153,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
   const int n_st = (cq1 - qs_al + QT - 1) / QT;
   const int n_it = p.G * n_st;
 
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float acc[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb][0] = acc[cb][1] = 0.f;
 
   // Direct-to-LDS loads: load k of this wave fills LDS chunks
   // [(wave*LOADS + k)*64, +64) of a stage, lane by lane.  Each lane fetches
@@ -188,7 +195,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
   auto write_partial = [&](int hp) {
     // the two lane halves hold complementary query rows of the same key
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       float tot = acc[cb][0] + acc[cb][1];
       tot += __shfl_xor(tot, 32);
       const int key = tw + 32 * cb + col;
@@ -200,9 +207,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
   auto half = [&](const char *ql, const float *nl, int q0) {
     // accumulators start at -L*log2(e) of the query row held by each
     // register (read twice from LDS rather than kept in a third tile)
-    f32x16 s[2];
+    f32x16 s[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl[8 * i4 + 4 * hf]);
@@ -213,18 +220,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) f
     for (int jj = 0; jj < NJ; ++jj) {
       Frag<T> a;
       read_a(a, ql, jj);
-      mma(s[0], a, kf[0][jj]);
-      mma(s[1], a, kf[1][jj]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) mma(s[cb], a, kf[cb][jj]);
     }
-    const bool interior = (q0 >= tw + 63 + w) && (q0 + 31 < n) && (tw + 63 < n);
+    const int tlast = tw + 32 * NCB - 1;
+    const bool interior = (q0 >= tlast + w) && (q0 + 31 < n) && (tlast < n);
     if (interior) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i]);
     } else {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         const int t = tw + 32 * cb + col;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
