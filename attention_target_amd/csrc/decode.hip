@@ -27,6 +27,10 @@
 namespace kvpop {
 
 constexpr int DEC_CHUNK = 128;  // slots per attention workgroup
+constexpr int DEC_WAVES = 16;   // waves per attention workgroup
+constexpr int DEC_ROWS = DEC_CHUNK / DEC_WAVES;  // slot rows per wave
+constexpr int DEC_MAX_SLOTS = 1 << 20;  // the C-ABI rejects larger caches
+constexpr int DEC_MAX_CHUNKS = DEC_MAX_SLOTS / DEC_CHUNK;  // merge weights held in LDS
 
 __device__ __forceinline__ uint64_t decode_key(float sc, int t) {
   if (sc != sc) sc = -INFINITY;
@@ -194,101 +198,226 @@ __global__ void __launch_bounds__(256) decode_update(DecParams p) {
   }
 }
 
-// Workgroup (chunk, b*Hkv + h): the G query heads of KV head h against slots
-// [chunk*DEC_CHUNK, +DEC_CHUNK).  Thread j owns slot j of the chunk for the
-// logits; the partial output is accumulated per (head, dimension).
+// Eight consecutive elements of a slot row, fetched with 16-byte loads.
 template <typename T>
-__global__ void __launch_bounds__(256) decode_attn(DecParams p) {
-  __shared__ float qs[8][256];           // up to 8 query heads, D <= 256
-  __shared__ float pr[8][DEC_CHUNK];     // probabilities of the chunk
-  __shared__ int vld[DEC_CHUNK];         // slot holds a retained token
-  __shared__ float red[8][4];
+struct Row8;
+template <>
+struct Row8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16 *src) { v = *reinterpret_cast<const bf16x8 *>(src); }
+  __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+};
+template <>
+struct Row8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float *src) {
+    a = *reinterpret_cast<const f32x4 *>(src);
+    b = *reinterpret_cast<const f32x4 *>(src + 4);
+  }
+  __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Sum over each aligned group of LPR (8 or 16) lanes, the total in every lane
+// of the group: two quad permutations, then the half-row and row mirrors,
+// each a DPP-modified add (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(LPR == 8 || LPR == 16, "lane groups of 8 or 16");
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x141>(x);  // row_half_mirror: lane i <- 7-i within 8
+  if constexpr (LPR == 16) x = dpp_add<0x140>(x);  // row_mirror: lane i <- 15-i within 16
+  return x;
+}
+
+// Workgroup (chunk, b*Hkv + h): the G query heads of KV head h against slots
+// [chunk*DEC_CHUNK, +DEC_CHUNK).  The kernel is bound by latency, not by
+// bandwidth or arithmetic, so the chunk is spread over DEC_WAVES waves of
+// DEC_ROWS rows each (two or more waves per SIMD), and every wave issues all
+// of its K, V and slot-position loads before it computes anything.  Lane l
+// covers 8 elements at 8*(l % LPR) of a slot row (LPR = D/8 lanes per row,
+// RPW = 64/LPR rows per load instruction).  Phases:
+//   1. logits: per-lane partial dot products finished by a DPP sum over the
+//      LPR lanes of a row, written to LDS (-inf for empty slots);
+//   2. one wave per query head reduces that head's maximum and sum of
+//      exponentials over the chunk;
+//   3. each wave forms its rows' probabilities and partial PV sums, reduced
+//      over the rows of the wave, then over the waves through LDS.
+// G (query heads per KV head) and D are template parameters so that register
+// arrays are indexed statically and every reduction is unrolled.
+template <typename T, int G, int D>
+__global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
+  constexpr int EPL = 8;                // elements per lane and row
+  constexpr int LPR = D / EPL;          // lanes per row: 16 (D=128) or 8 (D=64)
+  constexpr int RPW = 64 / LPR;         // rows per load instruction: 4 or 8
+  constexpr int NRG = DEC_ROWS / RPW;   // row groups per wave: 2 or 1
+  static_assert(DEC_ROWS % RPW == 0, "whole row groups per wave");
+  static_assert(G <= DEC_WAVES, "one wave per query head in phase 2");
+  __shared__ float lg[G][DEC_CHUNK];
+  __shared__ float ml[G][2];  // per head: maximum (log2 units) and sum
+  __shared__ float osum[DEC_WAVES][G][D];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = p.G, D = p.D;
+  const int r_in = lane / LPR, c = lane % LPR;
   const T *sk = reinterpret_cast<const T *>(p.st.k) + (size_t)bh * p.C * D;
   const T *sv = reinterpret_cast<const T *>(p.st.v) + (size_t)bh * p.C * D;
   const int *pos = p.st.pos + (size_t)bh * p.C;
-  for (int i = tid; i < G * D; i += 256) {
-    const int g = i / D, e = i % D;
-    qs[g][e] = (float)reinterpret_cast<const T *>(p.q)[((size_t)b * p.Hq + h * G + g) * D + e];
-  }
-  __syncthreads();
   const int j0 = chunk * DEC_CHUNK;
-  // logits (log2 units) of slot tid for every head; invalid slots are -inf
-  float lg[8];
-  const int slot = j0 + tid;
-  const bool valid = tid < DEC_CHUNK && slot < p.C && pos[slot] >= 0;
-  if (tid < DEC_CHUNK) vld[tid] = valid ? 1 : 0;
+  const int nslots = min(DEC_CHUNK, p.C - j0);
+
+  // every load of this wave, up front; rows past the chunk's end re-read
+  // its last row and are masked
+  Row8<T> kr[NRG], vr[NRG];
+  bool ok[NRG];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) lg[g] = -INFINITY;
-  if (valid) {
-    const T *kr = sk + (size_t)slot * D;
+  for (int i = 0; i < NRG; ++i) {
+    const int j = wave * DEC_ROWS + i * RPW + r_in;
+    const int jj = min(j, nslots - 1);
+    const size_t off = (size_t)(j0 + jj) * D + c * EPL;
+    kr[i].load(sk + off);
+    vr[i].load(sv + off);
+    ok[i] = j < nslots && pos[j0 + jj] >= 0;
+  }
+  float qv[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Row8<T> qr;
+    qr.load(reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + h * G + g) * D + c * EPL);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[g][e] = qr[e];
+  }
+
+  // 1. logits (log2 units)
+#pragma unroll
+  for (int i = 0; i < NRG; ++i) {
+    const int j = wave * DEC_ROWS + i * RPW + r_in;
+#pragma unroll
     for (int g = 0; g < G; ++g) {
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc += qs[g][e] * (float)kr[e];
-      lg[g] = acc * p.scale_log2;
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x += qv[g][e] * kr[i][e];
+      x = lane_group_sum<LPR>(x);
+      if (c == 0) lg[g][j] = ok[i] ? x * p.scale_log2 : -INFINITY;
     }
   }
-  // per-head max over the chunk
-  float mx[8];
-  for (int g = 0; g < G; ++g) {
-    float m = lg[g];
+  __syncthreads();
+
+  // 2. wave g: maximum and sum of exponentials of head g over the chunk
+  if (wave < G) {
+    const int g = wave;
+    const float x0 = lg[g][lane], x1 = lg[g][lane + 64];
+    float m = fmaxf(x0, x1);
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) red[g][wave] = m;
-  }
-  __syncthreads();
-  for (int g = 0; g < G; ++g) mx[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const float m = mx[g] == -INFINITY ? 0.f : mx[g];
-    const float pv = valid ? exp2f(lg[g] - m) : 0.f;
-    if (tid < DEC_CHUNK) pr[g][tid] = pv;
-    float l = pv;
+    const float mu = m == -INFINITY ? 0.f : m;
+    float l = exp2f(x0 - mu) + exp2f(x1 - mu);  // -inf: 0
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-    if (lane == 0) red[g][wave] = l;
+    if (lane == 0) {
+      ml[g][0] = m;
+      ml[g][1] = l;
+    }
   }
   __syncthreads();
-  // partial output: thread (g, e) sums over the chunk's slots in order
-  const int nslots = min(DEC_CHUNK, p.C - j0);
-  for (int i = tid; i < G * D; i += 256) {
+
+  // 3. probabilities and partial outputs; masked rows contribute zero
+  // whatever their V holds
+  float acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NRG; ++i) {
+    const int j = wave * DEC_ROWS + i * RPW + r_in;
+    float vf[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vf[e] = ok[i] ? vr[i][e] : 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m = ml[g][0];
+      const float pg = ok[i] ? exp2f(lg[g][j] - m) : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += pg * vf[e];
+    }
+  }
+  // reduce over the row groups of the wave (lanes with the same c)
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[g][e];
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) x += __shfl_xor(x, o);
+      acc[g][e] = x;
+    }
+  if (r_in == 0)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) osum[wave][g][c * EPL + e] = acc[g][e];
+  __syncthreads();
+  for (int i = tid; i < G * D; i += DEC_WAVES * 64) {
     const int g = i / D, e = i % D;
-    float acc = 0.f;
-    for (int j = 0; j < nslots; ++j)  // empty slots hold no data (possibly not even numbers)
-      if (vld[j]) acc += pr[g][j] * (float)sv[(size_t)(j0 + j) * D + e];
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) sum += osum[w][g][e];
     float *pp = p.st.part + (((size_t)b * p.Hq + h * G + g) * p.nchunk + chunk) * (D + 2);
-    pp[e] = acc;
+    pp[e] = sum;
     if (e == 0) {
-      pp[D] = mx[g];
-      pp[D + 1] = red[g][0] + red[g][1] + red[g][2] + red[g][3];
+      pp[D] = ml[g][0];
+      pp[D + 1] = ml[g][1];
     }
   }
 }
 
-// One workgroup per (b, query head): merge the chunks.
+// One workgroup per (b, query head): merge the chunks.  Chunk maxima and
+// sums are read by parallel threads into LDS and the merge weights computed
+// once; each thread then sums one output dimension over the chunks, eight
+// independent loads at a time.
 template <typename T>
 __global__ void __launch_bounds__(256) decode_combine(DecParams p) {
-  const int bg = blockIdx.x;
-  const int D = p.D;
-  const float *pp = p.st.part + (size_t)bg * p.nchunk * (D + 2);
+  __shared__ float wgt[DEC_MAX_CHUNKS];
+  __shared__ float red[4];
+  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = p.D, nc = p.nchunk;
+  const float *pp = p.st.part + (size_t)bg * nc * (D + 2);
   float m = -INFINITY;
-  for (int c = 0; c < p.nchunk; ++c) m = fmaxf(m, pp[c * (D + 2) + D]);
-  const float mu = m == -INFINITY ? 0.f : m;
-  float l = 0.f;
-  for (int c = 0; c < p.nchunk; ++c) {
-    const float mc = pp[c * (D + 2) + D];
-    if (mc != -INFINITY) l += pp[c * (D + 2) + D + 1] * exp2f(mc - mu);
+  for (int c = tid; c < nc; c += 256) {
+    const float mc = pp[(size_t)c * (D + 2) + D];
+    wgt[c] = mc;
+    m = fmaxf(m, mc);
   }
-  for (int e = threadIdx.x; e < D; e += 256) {
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float mu = m == -INFINITY ? 0.f : m;
+  __syncthreads();
+  float l = 0.f;
+  for (int c = tid; c < nc; c += 256) {
+    const float mc = wgt[c];
+    const float wc = mc == -INFINITY ? 0.f : exp2f(mc - mu);
+    wgt[c] = wc;
+    l += wc * pp[(size_t)c * (D + 2) + D + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  __syncthreads();  // every weight written before any thread reads them
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  l = red[0] + red[1] + red[2] + red[3];
+  for (int e = tid; e < D; e += 256) {
     float acc = 0.f;
-    for (int c = 0; c < p.nchunk; ++c) {
-      const float mc = pp[c * (D + 2) + D];
-      if (mc != -INFINITY) acc += pp[c * (D + 2) + e] * exp2f(mc - mu);
-    }
+#pragma unroll 8
+    for (int c = 0; c < nc; ++c) acc += pp[(size_t)c * (D + 2) + e] * wgt[c];
     reinterpret_cast<T *>(p.o)[(size_t)bg * D + e] = (T)(l > 0.f ? acc / l : 0.f);
   }
-  if (threadIdx.x == 0) p.lse[bg] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
+  if (tid == 0) p.lse[bg] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
 }
 
 static DecParams decode_params(const DecodeShapeInfo &s, void *state) {
@@ -316,10 +445,32 @@ hipError_t launch_decode_init(const DecodeShapeInfo &s, void *state, hipStream_t
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static bool launch_attn_g(const DecParams &p, dim3 grid, hipStream_t st) {
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((decode_attn<T, 1, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 2: hipLaunchKernelGGL((decode_attn<T, 2, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 3: hipLaunchKernelGGL((decode_attn<T, 3, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 4: hipLaunchKernelGGL((decode_attn<T, 4, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 5: hipLaunchKernelGGL((decode_attn<T, 5, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 6: hipLaunchKernelGGL((decode_attn<T, 6, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 7: hipLaunchKernelGGL((decode_attn<T, 7, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 8: hipLaunchKernelGGL((decode_attn<T, 8, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    default: return false;
+  }
+}
+
 template <typename T>
 static hipError_t run_decode(DecParams &p, hipStream_t st) {
   hipLaunchKernelGGL(decode_update<T>, dim3(p.B * p.Hkv), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(decode_attn<T>, dim3(p.nchunk, p.B * p.Hkv), dim3(256), 0, st, p);
+  const dim3 grid(p.nchunk, p.B * p.Hkv);
+  if (p.D == 128) {
+    if (!launch_attn_g<T, 128>(p, grid, st)) return hipErrorInvalidValue;
+  } else if (p.D == 64) {
+    if (!launch_attn_g<T, 64>(p, grid, st)) return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(decode_combine<T>, dim3(p.B * p.Hq), dim3(256), 0, st, p);
   return hipGetLastError();
 }

@@ -32,6 +32,10 @@ CASES = [
     (260, 2, 1, 64, "f32", 3, 8, 0),        # k = 0: sinks and window only
     (150, 4, 1, 128, "bf16", 4, 64, 300),   # budget larger than the sequence: dense causal
     (700, 4, 1, 128, "bf16", 4, 128, 200),  # several attention chunks
+    (220, 8, 1, 128, "bf16", 2, 16, 40),    # 8 query heads per KV head
+    (180, 3, 3, 64, "f32", 1, 8, 25),       # one query head per KV head
+    (240, 6, 2, 128, "bf16", 4, 16, 60),    # 3 query heads per KV head
+    (1300, 2, 1, 64, "bf16", 4, 64, 1100),  # ten chunks, the last one ragged
 ]
 
 
