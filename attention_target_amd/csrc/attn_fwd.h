@@ -302,14 +302,20 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
         }
       }
 
-      // masked row maximum of the raw logits
+      // masked row maximum of the raw logits (one uniform branch around two
+      // straight-line loops: a test per element would become a branch per
+      // element)
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[rb][i];
-          if (!full) {
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
             const int r = 32 * rb + c_row(i, hf);
             bool ok;
             if constexpr (!SPARSE) {
@@ -320,10 +326,10 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
               const int rk = krank_lds[buf][r];
               ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
             }
-            x = ok ? x : -INFINITY;
+            const float x = ok ? s[rb][i] : -INFINITY;
+            s[rb][i] = x;
+            mx = fmaxf(mx, x);
           }
-          s[rb][i] = x;
-          mx = fmaxf(mx, x);
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));

@@ -37,7 +37,7 @@ constexpr int CUT_ALL = 2147483647;
 constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
-  size_t keys, sorted, rank, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, total;
+  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
 
@@ -66,6 +66,7 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   lo.keys = take(BH * lo.S_pad * 8);
   lo.sorted = take(BH * lo.S_pad * 8);
   lo.rank = take(BH * s.S * 4);
+  lo.order = take(BH * s.S * 4);
   lo.cutoff = take(BH * s.S * 4);
   lo.arr0 = take(BH * s.S * 4);
   lo.arr1 = take(BH * s.S * 4);
@@ -245,6 +246,12 @@ constexpr int WV_LDS_MAX = 32768;  // eligible tokens per (batch, KV head)
 constexpr int WV_LDS_WORDS = WV_LDS_MAX / 32 + 32;
 
 __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletParams p) {
+  // Thread tid holds elements tid + 1024*j (j < WV_PER_THREAD), so the 64
+  // elements of one ballot are consecutive and give two bit words at once.
+  // Each level loads all of a thread's values first (independent LDS reads
+  // in flight together), keeps its ballot masks in registers for the
+  // scatter, and needs three barriers.
+  constexpr int WV_PER_THREAD = WV_LDS_MAX / 1024;
   __shared__ uint16_t arr[2][WV_LDS_MAX];
   __shared__ uint32_t wl[WV_LDS_WORDS];
   __shared__ int pl_s[WV_LDS_WORDS];
@@ -254,22 +261,39 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
   const int n_e = p.S - p.sinks;
   if (n_e <= 0 || n_e > WV_LDS_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
   for (int i = tid; i < n_e; i += 1024) arr[0][i] = (uint16_t)p.rank[bh * p.S + p.sinks + i];
+  const int nj = (n_e + 1023) / 1024;
+  const int w_end = 32 * nj;  // words written by the ballots; [w_end, nw1) stay zero
+  for (int w = w_end + tid; w < p.nw1; w += 1024) wl[w] = 0u;
   __syncthreads();
   const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
+  const uint64_t below = lanemask_lt(lane);
   int cur = 0;
   for (int lvl = p.L - 1; lvl >= 0; --lvl) {
     const uint16_t *a = arr[cur];
     uint16_t *b = arr[cur ^ 1];
     uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
     int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
-    // bit words: one ballot gives the two words of 64 consecutive elements
-    for (int base = 0; base < 32 * p.nw1; base += 1024) {
-      const int i = base + tid;
-      const int bit = (i < n_e) ? ((a[i] >> lvl) & 1) : 0;
-      const uint64_t m = __ballot(bit);
-      const int w0 = (base + 64 * wave) / 32;
-      if (lane == 0 && w0 < p.nw1) wl[w0] = (uint32_t)m;
-      if (lane == 0 && w0 + 1 < p.nw1) wl[w0 + 1] = (uint32_t)(m >> 32);
+    int val[WV_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) {
+      const int i = tid + 1024 * j;
+      val[j] = (j < nj && i < n_e) ? (int)a[i] : -1;
+    }
+    // bit words, and each element's count of ones before it in its 64
+    uint32_t bits_mine = 0;
+    int before_w[WV_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) {
+      if (j < nj) {
+        const int bit = val[j] >= 0 ? (val[j] >> lvl) & 1 : 0;
+        const uint64_t m = __ballot(bit);
+        bits_mine |= (uint32_t)bit << j;
+        before_w[j] = __popcll(m & below);
+        if (lane == 0) {
+          wl[32 * j + 2 * wave] = (uint32_t)m;
+          wl[32 * j + 2 * wave + 1] = (uint32_t)(m >> 32);
+        }
+      }
     }
     __syncthreads();
     int local = 0;
@@ -292,12 +316,14 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
     if (tid == 0) p.zeros[bh * p.L + lvl] = Z;
     __syncthreads();
     // stable partition: zeros first, then ones
-    for (int i = tid; i < n_e; i += 1024) {
-      const int v = a[i];
-      const int w = i >> 5;
-      const int before = pl_s[w] + __popc(wl[w] & ((1u << (i & 31)) - 1u));
-      const int pos = ((v >> lvl) & 1) ? Z + before : i - before;
-      if (pos >= 0 && pos < n_e) b[pos] = (uint16_t)v;
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) {
+      const int i = tid + 1024 * j;
+      if (j < nj && i < n_e) {
+        const int before = pl_s[32 * j + 2 * wave] + before_w[j];  // ones before element i
+        const int pos = ((bits_mine >> j) & 1) ? Z + before : i - before;
+        if (pos >= 0 && pos < n_e) b[pos] = (uint16_t)val[j];
+      }
     }
     __syncthreads();
     cur ^= 1;
@@ -343,13 +369,22 @@ __global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int
   cutoff[bh * p.S + d] = res;
 }
 
+// Inverse of the rank permutation: order[r] = the token of rank r.
+__global__ void __launch_bounds__(256) rank_order(const int *rank, int *order, int S) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  if (t >= S) return;
+  const int r = rank[bh * S + t];
+  if (r >= 0 && r < S) order[bh * S + r] = t;
+}
+
 struct ListParams {
-  const int *rank, *cutoff;
+  const int *rank, *order, *cutoff;
   int *lists, *lens, *lens_full;
   int S, sinks, window, topk, QB, nqb, cap;
 };
 
-// Key list of query block [d0, d1], in two ascending segments:
+// Key list of query block [d0, d1], in two segments:
 //   full:    the sinks below the window, then the eligible tokens of
 //            [s, d0-w] with rank <= c_{d1}.  Every query of the block keeps
 //            all of them (c_d is non-increasing, so c_{d1} <= c_d), so
@@ -359,6 +394,10 @@ struct ListParams {
 // The size of the full segment is known before the sweep: E_{d1} holds
 // exactly topk tokens of rank <= c_{d1}, so E_{d0} holds topk minus those in
 // (d0-w, d1-w] (at most QB-1 reads).
+// The eligible tokens are found by whichever sweep is shorter: over the
+// positions [s, d0-w], or over the ranks [0, c_{d0}] through the inverse
+// permutation (late blocks: c_{d0} is about topk while d0-w grows with d0).
+// The attention kernel needs no order inside a segment.
 __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   __shared__ int sh_w[2][4];
   __shared__ int sh_sub;
@@ -369,6 +408,7 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   const int c0 = p.cutoff[bh * p.S + d0];
   const int c1 = p.cutoff[bh * p.S + d1];
   const int *rk = p.rank + bh * p.S;
+  const int *ord = p.order + bh * p.S;
   int *list = p.lists + (bh * p.nqb + qb) * (size_t)p.cap;
   const int a_end = max(0, min(min(p.sinks, d0 - p.window + 1), d1 + 1));
   const int b_hi = d0 - p.window;  // E_{d0} = [sinks, b_hi]
@@ -390,11 +430,24 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   const int n_full = a_end + n_bfull;
   for (int i = tid; i < a_end && i < p.cap; i += 256) list[i] = i;
   int off_f = a_end, off_p = n_full;
-  for (int base = p.sinks; base <= b_hi; base += 256) {
-    const int t = base + tid;
-    const int r = (t <= b_hi) ? rk[t] : INT32_MAX;
-    const bool ff = (t <= b_hi) && r <= c1;
-    const bool fp = (t <= b_hi) && r > c1 && r <= c0;
+  // sweep length: positions [s, b_hi], or ranks [0, c0]
+  const bool by_rank = c0 != CUT_NONE && c0 != CUT_ALL && c0 + 1 < n_e0;
+  const int n_sweep = c0 == CUT_NONE ? 0 : (by_rank ? c0 + 1 : n_e0);
+  for (int base = 0; base < n_sweep; base += 256) {
+    const int x = base + tid;
+    int t = -1, r = INT32_MAX;
+    if (x < n_sweep) {
+      if (by_rank) {
+        r = x;
+        t = ord[x];
+      } else {
+        t = p.sinks + x;
+        r = rk[t];
+      }
+    }
+    const bool elig = t >= p.sinks && t <= b_hi;
+    const bool ff = elig && r <= c1;
+    const bool fp = elig && r > c1 && r <= c0;
     const uint64_t mf = __ballot(ff), mp = __ballot(fp);
     if (lane == 0) {
       sh_w[0][wave] = __popcll(mf);
@@ -475,8 +528,11 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  int *order = reinterpret_cast<int *>(w + lo.order);
+  hipLaunchKernelGGL(rank_order, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, rank, order, s.S);
   ListParams lp{};
   lp.rank = rank;
+  lp.order = order;
   lp.cutoff = cutoff;
   lp.lists = reinterpret_cast<int *>(w + lo.lists);
   lp.lens = reinterpret_cast<int *>(w + lo.lens);
@@ -548,14 +604,6 @@ __global__ void __launch_bounds__(256) teacher_keys(const float *y, const float 
     key = score_key(pri, t);
   }
   keys[bh * S_pad + t] = key;
-}
-
-__global__ void __launch_bounds__(256) teacher_order(const int *rank, int *order, int S) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const size_t bh = blockIdx.y;
-  if (t >= S) return;
-  const int r = rank[bh * S + t];
-  if (r >= 0 && r < S) order[bh * S + r] = t;
 }
 
 struct TeacherParams {
@@ -630,7 +678,7 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   hipLaunchKernelGGL(teacher_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, y, lam, delta, keys, S, lo.S_pad, Hkv);
   hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(256), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
   hipLaunchKernelGGL(budget_rank, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, S, lo.S_pad, lo.nchunks);
-  hipLaunchKernelGGL(teacher_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
+  hipLaunchKernelGGL(rank_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TeacherParams tp{};
