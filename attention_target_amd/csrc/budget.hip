@@ -724,7 +724,11 @@ struct LossParams {
   const float *pred, *weight;
   const int *label, *boundary;
   float *loss, *grad, *gterm, *slot0, *slot1;
-  int S, window, dstar;
+  float *segsum;  // [BH][S]: in-wave sum of the segment a head lane starts
+  int *wf_b;      // [BH][nwv]: boundary of each 64-position wave's first element
+  int *wf_whole;  // [BH][nwv]: whether that wave is one segment
+  float *wf_sum;  // [BH][nwv]: sum of the wave's first segment
+  int S, window, dstar, nwv;
   float inv_tau;
 };
 
@@ -750,15 +754,81 @@ __global__ void __launch_bounds__(256) boundary_loss_terms(const LossParams p) {
   p.slot1[i] = 0.f;
 }
 
+// The gradient of a boundary token b collects the terms of the consecutive
+// positions d whose boundary is b (a run).  Sums in a fixed order (so the
+// result is reproducible), in two levels: each wave of 64 positions forms
+// the sum of every segment of equal boundary inside it by a segmented
+// suffix scan, and records its first segment; the head of a run then adds
+// the first segments of the following waves while the run continues.
+__device__ __forceinline__ int loss_boundary_at(const LossParams &p, size_t bh, int d) {
+  if (d >= p.S) return -2;
+  const int b = p.boundary[bh * p.S + d];
+  return (b >= 0 && b < p.S) ? b : -1;
+}
+
+__global__ void __launch_bounds__(256) boundary_loss_segments(const LossParams p) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const size_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int b = loss_boundary_at(p, bh, d);
+  float x = (d < p.S) ? p.gterm[bh * p.S + d] : 0.f;
+  const int b_up = __shfl_up(b, 1);
+  const bool head = lane == 0 || b != b_up;
+  const uint64_t H = __ballot(head);
+  const uint64_t above = lane == 63 ? 0ull : (H & (~0ull << (lane + 1)));
+  const int end = above ? __ffsll((long long)above) - 1 : 64;  // first lane of the next segment
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_down(x, o);
+    if (lane + o < end) x += y;
+  }
+  if (d < p.S && head) p.segsum[bh * p.S + d] = x;
+  if (lane == 0 && d < p.S) {
+    const size_t w = bh * p.nwv + d / 64;
+    p.wf_b[w] = b;
+    p.wf_whole[w] = H == 1ull;
+    p.wf_sum[w] = x;
+  }
+}
+
 __global__ void __launch_bounds__(256) boundary_loss_runs(const LossParams p) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   const size_t bh = blockIdx.y;
-  if (d >= p.S) return;
-  const int *bd = p.boundary + bh * p.S;
-  const int b = bd[d];
-  if (b < 0 || b >= p.S || (d > 0 && bd[d - 1] == b)) return;  // not the first d of a run
-  float sum = 0.f;
-  for (int e = d; e < p.S && bd[e] == b; ++e) sum += p.gterm[bh * p.S + e];
+  const int lane = threadIdx.x & 63;
+  const int b = loss_boundary_at(p, bh, d);
+  const int b_up = __shfl_up(b, 1);
+  const bool head = lane == 0 || b != b_up;
+  const uint64_t H = __ballot(head);
+  if (d >= p.S || b < 0 || !head) return;
+  if (lane == 0 && d > 0 && loss_boundary_at(p, bh, d - 1) == b) return;  // continues the previous wave's run
+  float sum = p.segsum[bh * p.S + d];
+  const uint64_t above = lane == 63 ? 0ull : (H & (~0ull << (lane + 1)));
+  if (above == 0ull) {  // the segment reaches the end of its wave: follow the run
+    bool go = true;
+    for (int w0 = d / 64 + 1; go && w0 < p.nwv; w0 += 8) {
+      int fb[8], fw[8];
+      float fs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = w0 + j;
+        const size_t i = bh * p.nwv + min(w, p.nwv - 1);
+        fb[j] = w < p.nwv ? p.wf_b[i] : -3;
+        fw[j] = p.wf_whole[i];
+        fs[j] = p.wf_sum[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (go) {
+          if (fb[j] != b) {
+            go = false;
+          } else {
+            sum += fs[j];
+            if (!fw[j]) go = false;
+          }
+        }
+      }
+    }
+  }
   float *slot = (d < p.dstar) ? p.slot0 : p.slot1;
   slot[bh * p.S + b] = sum;
 }
@@ -772,7 +842,12 @@ __global__ void __launch_bounds__(256) boundary_loss_grad(const LossParams p) {
   p.grad[i] = g_new - p.slot0[i] - p.slot1[i];
 }
 
-size_t boundary_loss_workspace_bytes(int B, int Hkv, int S) { return 3 * al256((size_t)B * Hkv * S * 4); }
+static int loss_waves(int S) { return (S + 63) / 64; }
+
+size_t boundary_loss_workspace_bytes(int B, int Hkv, int S) {
+  const size_t BH = (size_t)B * Hkv;
+  return 4 * al256(BH * S * 4) + 3 * al256(BH * loss_waves(S) * 4);
+}
 
 hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const int *label, const int *boundary,
                                 int sinks, int window, int topk, float tau, const float *weight, float *loss,
@@ -786,9 +861,15 @@ hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const 
   lp.boundary = boundary;
   lp.loss = loss;
   lp.grad = grad;
+  const size_t nw = al256((size_t)B * Hkv * loss_waves(S) * 4);
   lp.gterm = reinterpret_cast<float *>(w);
   lp.slot0 = reinterpret_cast<float *>(w + n);
   lp.slot1 = reinterpret_cast<float *>(w + 2 * n);
+  lp.segsum = reinterpret_cast<float *>(w + 3 * n);
+  lp.wf_b = reinterpret_cast<int *>(w + 4 * n);
+  lp.wf_whole = reinterpret_cast<int *>(w + 4 * n + nw);
+  lp.wf_sum = reinterpret_cast<float *>(w + 4 * n + 2 * nw);
+  lp.nwv = loss_waves(S);
   lp.S = S;
   lp.window = window;
   const long long ds = (long long)sinks + window + topk - 1;
@@ -796,6 +877,7 @@ hipError_t launch_boundary_loss(int B, int Hkv, int S, const float *pred, const 
   lp.inv_tau = 1.f / tau;
   const dim3 grid((S + 255) / 256, B * Hkv);
   hipLaunchKernelGGL(boundary_loss_terms, grid, dim3(256), 0, st, lp);
+  hipLaunchKernelGGL(boundary_loss_segments, grid, dim3(256), 0, st, lp);
   hipLaunchKernelGGL(boundary_loss_runs, grid, dim3(256), 0, st, lp);
   hipLaunchKernelGGL(boundary_loss_grad, grid, dim3(256), 0, st, lp);
   return hipGetLastError();

@@ -105,7 +105,9 @@ def check_loss(kv, y, s, w, k, tau, with_weight, seed):
 
 
 @pytest.mark.parametrize("S,s,w,k,tau,wt", [(500, 4, 16, 40, 1.0, False), (3000, 2, 64, 300, 0.5, True),
-                                            (200, 4, 8, 500, 2.0, True)])
+                                            (200, 4, 8, 500, 2.0, True),
+                                            # long runs of one boundary token across many 64-position waves
+                                            (5000, 4, 32, 2000, 1.0, False), (4096, 0, 64, 1000, 0.5, True)])
 def test_boundary_loss_and_gradient(kvpop_lib, S, s, w, k, tau, wt):
     say(f"boundary loss S={S} s={s} w={w} k={k} tau={tau} weight={wt}")
     y = make_y(1, 2, S, "normal", 7 * S)
