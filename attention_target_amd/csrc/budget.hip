@@ -248,11 +248,13 @@ constexpr int WV_LDS_WORDS = WV_LDS_MAX / 32 + 32;
 __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletParams p) {
   // Thread tid holds elements tid + 1024*j (j < WV_PER_THREAD), so the 64
   // elements of one ballot are consecutive and give two bit words at once.
-  // Each level loads all of a thread's values first (independent LDS reads
-  // in flight together), keeps its ballot masks in registers for the
-  // scatter, and needs three barriers.
+  // The level body is straight-line code: a thread's values are read
+  // together and kept two per register, slots past n_e take part with bit 0
+  // and scatter into a small dummy area, and the bit words are stored by
+  // all lanes of a wave (two addresses, consistent data) instead of under a
+  // lane test.
   constexpr int WV_PER_THREAD = WV_LDS_MAX / 1024;
-  __shared__ uint16_t arr[2][WV_LDS_MAX];
+  __shared__ uint16_t arr[2][WV_LDS_MAX + 64];
   __shared__ uint32_t wl[WV_LDS_WORDS];
   __shared__ int pl_s[WV_LDS_WORDS];
   __shared__ int sh_waves[16];
@@ -260,40 +262,38 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_e = p.S - p.sinks;
   if (n_e <= 0 || n_e > WV_LDS_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
-  for (int i = tid; i < n_e; i += 1024) arr[0][i] = (uint16_t)p.rank[bh * p.S + p.sinks + i];
-  const int nj = (n_e + 1023) / 1024;
-  const int w_end = 32 * nj;  // words written by the ballots; [w_end, nw1) stay zero
-  for (int w = w_end + tid; w < p.nw1; w += 1024) wl[w] = 0u;
+  {
+    const int *src = p.rank + bh * p.S + p.sinks;
+    int r[WV_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) r[j] = src[min(tid + 1024 * j, n_e - 1)];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) arr[0][tid + 1024 * j] = (uint16_t)r[j];
+  }
+  for (int w = 32 * WV_PER_THREAD + tid; w < p.nw1; w += 1024) wl[w] = 0u;  // words past the ballots' reach
   __syncthreads();
   const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
-  const uint64_t below = lanemask_lt(lane);
   int cur = 0;
   for (int lvl = p.L - 1; lvl >= 0; --lvl) {
     const uint16_t *a = arr[cur];
     uint16_t *b = arr[cur ^ 1];
     uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
     int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
-    int val[WV_PER_THREAD];
+    // An opaque copy of the thread index: element indices are then formed in
+    // place each level rather than kept live across the level loop.
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    // values two per register
+    uint32_t val2[WV_PER_THREAD / 2];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; j += 2)
+      val2[j / 2] = (uint32_t)a[t + 1024 * j] | ((uint32_t)a[t + 1024 * (j + 1)] << 16);
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      const int i = tid + 1024 * j;
-      val[j] = (j < nj && i < n_e) ? (int)a[i] : -1;
-    }
-    // bit words, and each element's count of ones before it in its 64
-    uint32_t bits_mine = 0;
-    int before_w[WV_PER_THREAD];
-#pragma unroll
-    for (int j = 0; j < WV_PER_THREAD; ++j) {
-      if (j < nj) {
-        const int bit = val[j] >= 0 ? (val[j] >> lvl) & 1 : 0;
-        const uint64_t m = __ballot(bit);
-        bits_mine |= (uint32_t)bit << j;
-        before_w[j] = __popcll(m & below);
-        if (lane == 0) {
-          wl[32 * j + 2 * wave] = (uint32_t)m;
-          wl[32 * j + 2 * wave + 1] = (uint32_t)(m >> 32);
-        }
-      }
+      const uint32_t v = (val2[j / 2] >> (16 * (j & 1))) & 0xffffu;
+      const int bit = (t + 1024 * j < n_e) ? (int)(v >> lvl) & 1 : 0;
+      const uint64_t m = __ballot(bit);
+      wl[32 * j + 2 * wave + (lane & 1)] = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
     }
     __syncthreads();
     int local = 0;
@@ -315,15 +315,18 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
     const int Z = n_e - ones;
     if (tid == 0) p.zeros[bh * p.L + lvl] = Z;
     __syncthreads();
-    // stable partition: zeros first, then ones
+    // stable partition: zeros first, then ones; the count of ones before an
+    // element comes from its bit word (one broadcast read per half wave)
+    const uint32_t below32 = (1u << (lane & 31)) - 1u;
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      const int i = tid + 1024 * j;
-      if (j < nj && i < n_e) {
-        const int before = pl_s[32 * j + 2 * wave] + before_w[j];  // ones before element i
-        const int pos = ((bits_mine >> j) & 1) ? Z + before : i - before;
-        if (pos >= 0 && pos < n_e) b[pos] = (uint16_t)val[j];
-      }
+      const int i = t + 1024 * j;
+      const int w = 32 * j + 2 * wave + (lane >> 5);  // == i >> 5
+      const uint32_t word = wl[w];
+      const int before = pl_s[w] + __popc(word & below32);
+      int pos = ((word >> (lane & 31)) & 1) ? Z + before : i - before;
+      pos = (i < n_e && pos >= 0 && pos < n_e) ? pos : WV_LDS_MAX + lane;
+      b[pos] = (uint16_t)(val2[j / 2] >> (16 * (j & 1)));
     }
     __syncthreads();
     cur ^= 1;
