@@ -105,47 +105,69 @@ __global__ void __launch_bounds__(256) budget_keys(const float *scores, uint64_t
   keys[bh * S_pad + t] = (t < S) ? score_key(scores[bh * S + t], t) : ~0ull;
 }
 
-__global__ void __launch_bounds__(256) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad, int nchunks) {
+// Bitonic sort of one 2048-key chunk in LDS; 1024 threads, so every stage
+// is one compare-exchange per thread.
+__global__ void __launch_bounds__(1024) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad, int nchunks) {
+  static_assert(RANK_CH == 2048, "one compare-exchange per thread and stage");
   __shared__ uint64_t sh[RANK_CH];
   const size_t base = (size_t)blockIdx.y * S_pad + (size_t)blockIdx.x * RANK_CH;
-  for (int i = threadIdx.x; i < RANK_CH; i += 256) sh[i] = keys[base + i];
+  const int tid = threadIdx.x;
+  sh[tid] = keys[base + tid];
+  sh[tid + 1024] = keys[base + tid + 1024];
   __syncthreads();
   for (int k = 2; k <= RANK_CH; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < RANK_CH; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const bool up = (i & k) == 0;
-          const uint64_t a = sh[i], b = sh[ixj];
-          if ((a > b) == up) {
-            sh[i] = b;
-            sh[ixj] = a;
-          }
-        }
+      const int i = 2 * tid - (tid & (j - 1));  // the lower index of this thread's pair
+      const int ixj = i + j;
+      const bool up = (i & k) == 0;
+      const uint64_t a = sh[i], b = sh[ixj];
+      if ((a > b) == up) {
+        sh[i] = b;
+        sh[ixj] = a;
       }
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < RANK_CH; i += 256) sorted[base + i] = sh[i];
+  sorted[base + tid] = sh[tid];
+  sorted[base + tid + 1024] = sh[tid + 1024];
 }
 
+// rank(t) = the number of keys below key(t), summed over the sorted chunks.
+// A workgroup ranks 256 tokens: it stages one sorted chunk at a time in LDS
+// (coalesced, double-buffered, the next chunk's loads in flight during the
+// current search) and each thread runs a branch-free lower-bound search of
+// fixed depth there, instead of scattered probes through L2.
 __global__ void __launch_bounds__(256) budget_rank(const uint64_t *keys, const uint64_t *sorted, int *rank,
                                                    int S, int S_pad, int nchunks) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  __shared__ uint64_t ch[2][RANK_CH];
+  constexpr int PER = RANK_CH / 256;
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * 256 + tid;
   const size_t bh = blockIdx.y;
-  if (t >= S) return;
-  const uint64_t key = keys[bh * S_pad + t];
+  const uint64_t key = keys[bh * S_pad + min(t, S_pad - 1)];
+  const uint64_t *srt = sorted + bh * S_pad;
+  uint64_t stage[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) stage[e] = srt[tid + 256 * e];
   int cnt = 0;
   for (int c = 0; c < nchunks; ++c) {
-    const uint64_t *a = sorted + bh * S_pad + (size_t)c * RANK_CH;
-    int lo = 0, hi = RANK_CH;  // first index with a[i] >= key
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a[mid] < key) lo = mid + 1; else hi = mid;
+    uint64_t *buf = ch[c & 1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) buf[tid + 256 * e] = stage[e];
+    __syncthreads();
+    if (c + 1 < nchunks) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) stage[e] = srt[(size_t)(c + 1) * RANK_CH + tid + 256 * e];
     }
-    cnt += lo;
+    int lo = 0;
+#pragma unroll
+    for (int step = RANK_CH / 2; step > 0; step >>= 1)
+      if (buf[lo + step - 1] < key) lo += step;
+    cnt += lo + (buf[lo] < key ? 1 : 0);
+    // the buffer written next iteration is the other one; a barrier there
+    // (after its writes) orders them against this iteration's reads of it
   }
-  rank[bh * S + t] = cnt;
+  if (t < S) rank[bh * S + t] = cnt;
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads).
@@ -505,7 +527,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   int *cutoff = cutoff_out ? cutoff_out : reinterpret_cast<int *>(w + lo.cutoff);
 
   hipLaunchKernelGGL(budget_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, scores, keys, s.S, lo.S_pad);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(256), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
   hipLaunchKernelGGL(budget_rank, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, s.S, lo.S_pad, lo.nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -679,7 +701,7 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
   int *order = reinterpret_cast<int *>(w + lo.order);
   hipLaunchKernelGGL(teacher_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, y, lam, delta, keys, S, lo.S_pad, Hkv);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(256), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
   hipLaunchKernelGGL(budget_rank, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, S, lo.S_pad, lo.nchunks);
   hipLaunchKernelGGL(rank_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
   hipError_t e = hipGetLastError();
