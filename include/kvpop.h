@@ -235,7 +235,10 @@ size_t kvpop_boundary_loss_workspace_size(int32_t batch, int32_t n_kv_heads, int
  *  q [B,Hq,D], k, v [B,Hkv,D]   the new token (dtype)
  *  score [B,Hkv] fp32           its static priority
  *  o [B,Hq,D] (dtype), lse [B,Hq] fp32   outputs
- * At most 8 query heads per KV head; head_dim 64 or 128.
+ * At most 8 query heads per KV head (else KVPOP_EUNSUPPORTED); head_dim 64
+ * or 128; 1 <= sinks + window + topk <= 2^20 slots (more: KVPOP_EUNSUPPORTED).
+ * A state too small for the shape gives KVPOP_EWORKSPACE.  Steps on one
+ * state must be ordered (one stream); concurrent steps on one state race.
  */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
