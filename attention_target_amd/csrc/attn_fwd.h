@@ -265,7 +265,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
       fetch_dense(0, 0);
     }
   }
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // One tile: wait for its loads, publish them with a barrier (which also
+  // retires every read of the other buffer), start the next tile's loads,
+  // then compute.  FULL tiles need no element mask.  Tiles of each kind form
+  // contiguous ranges, so each kind runs in a loop of its own with
+  // straight-line code (a per-tile choice would merge the two paths' S tiles
+  // and cost a register copy of both per tile).
+  auto tile_step = [&](int tile, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
     const int buf = tile & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -279,14 +286,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     }
 
     // Which of this wave's elements can be valid in this tile?
-    bool any = wave_active, full = false;
+    bool any = wave_active;
     const int tb = kbeg + tile * KT;
-    if constexpr (!SPARSE) {
-      any = any && tb <= wq_last && tb + KT - 1 >= wds_first;
-      full = tb >= wds_last && tb + KT - 1 <= q0 && tb + KT - 1 < kend;
-    } else {
-      full = tile < full_tiles;
-    }
+    if constexpr (!SPARSE) any = any && tb <= wq_last && tb + KT - 1 >= wds_first;
     if (any) {
       const char *kl = smem[buf];
       const char *vl = smem[buf] + Tiles::K_BYTES;
@@ -302,11 +304,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
         }
       }
 
-      // masked row maximum of the raw logits (one uniform branch around two
-      // straight-line loops: a test per element would become a branch per
-      // element)
+      // masked row maximum of the raw logits
       float mx = -INFINITY;
-      if (full) {
+      if constexpr (FULL) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -382,7 +382,21 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     if constexpr (SPARSE) {
       if (tile + 1 < n_tiles) store_pos(buf ^ 1);
     }
+
+  };
+  int f0 = 0, f1 = 0;  // the unmasked tiles are [f0, f1)
+  if constexpr (SPARSE) {
+    f1 = full_tiles;
+  } else {
+    // tb >= wds_last, tb + KT - 1 <= q0 and tb + KT - 1 < kend, tb = kbeg + tile * KT
+    f0 = max(0, (wds_last - kbeg + KT - 1) / KT);
+    const int last = min(q0, kend - 1) - (KT - 1) - kbeg;  // tb - kbeg <= last
+    f1 = last >= 0 ? min(n_tiles, last / KT + 1) : 0;
+    f1 = max(f1, f0);
   }
+  for (int tile = 0; tile < f0; ++tile) tile_step(tile, std::false_type{});
+  for (int tile = f0; tile < f1; ++tile) tile_step(tile, std::true_type{});
+  for (int tile = f1; tile < n_tiles; ++tile) tile_step(tile, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
