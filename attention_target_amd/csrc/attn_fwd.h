@@ -41,9 +41,16 @@ struct FwdParams {
   int list_cap, sinks, window;
 };
 
+#ifndef KVPOP_FWD_KT
+#define KVPOP_FWD_KT 64
+#endif
+#ifndef KVPOP_FWD_WAVES
+#define KVPOP_FWD_WAVES 2
+#endif
+
 template <typename T, int D>
 struct FwdTiles {
-  static constexpr int KT = 64;                           // keys per tile
+  static constexpr int KT = KVPOP_FWD_KT;                 // keys per tile
   static constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                     // 16-byte chunks per row
   static constexpr int ROWB = D * (int)sizeof(T);         // bytes per row
@@ -107,12 +114,13 @@ __device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int, int
 }
 
 template <typename T, int D, bool WITH_O, bool SPARSE>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_FWD_WAVES))) attn_fwd_kernel(const FwdParams p) {
   using Tiles = FwdTiles<T, D>;
   using KTile = SwizzledTile<T, D>;
   constexpr int NJ = D / 16;  // k-steps over the head dimension
   constexpr int NB = D / 32;  // 32-dim blocks of O^T
   constexpr int KT = Tiles::KT;
+  constexpr int NRB = KT / 32;  // 32-key row blocks of S^T per tile
   constexpr int EPC = Tiles::EPC;
   constexpr int CPR = Tiles::CPR;
   constexpr int ROWB = Tiles::ROWB;
@@ -292,9 +300,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
     if (any) {
       const char *kl = smem[buf];
       const char *vl = smem[buf] + Tiles::K_BYTES;
-      f32x16 s[2];
+      f32x16 s[NRB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
         s[rb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -308,12 +316,12 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
       float mx = -INFINITY;
       if constexpr (FULL) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
       } else {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = 32 * rb + c_row(i, hf);
@@ -347,7 +355,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, -m_use));
@@ -358,7 +366,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const FwdParams p) {
 
       if constexpr (WITH_O) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < KT / 16; ++j) {
           Frag<T> pf;
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
