@@ -2,35 +2,53 @@
 //
 // KVpop paper, Section 3: every KV head keeps s sink tokens, a protected
 // window of the w most recent tokens, and the k best eligible tokens by
-// static priority, so the per-head cache never exceeds B = s + w + k slots
+// static priority, so the per-head cache never exceeds B = s + w + k tokens
 // (Section 4.3 measures the resulting flat memory at decode time).  Each
 // step (Section 3.2, "Running top-k sparse attention"): the new token enters
 // the window; token d-w leaves it and competes for the top-k; if the top-k is
 // full and the newcomer beats the worst retained token, that token is
 // evicted for good (with static priorities a dropped token can never return:
 // the set of better tokens only grows).  The query then attends over the
-// retained slots, which are exactly the budget mask's row d.
+// retained tokens, which are exactly the budget mask's row d.
 //
 // State per (batch row, KV head), caller-owned device memory:
-//   slot K, V   [C, D] (C = s + w + k): slots [0, s) sinks, [s, s+w) the
-//               window ring (token t >= s at s + t mod w), [s+w, C) the
-//               top-k set in no particular order;
-//   slot pos    [C] int32, -1 when empty;  slot key [C] uint64, the
-//               order key (descending priority, then ascending index);
-//   topk count  int32.
-// Kernels: decode_update (one workgroup per (b, h)), decode_attn (split
-// over slot chunks, G query heads per workgroup, fp32 online softmax),
-// decode_combine (merges the chunks per query head).
+//   slot K, V   [C, D], C = s + R + k with R = w + 1 ring slots (0 if w = 0):
+//               slots [0, s) sinks, [s, s+R) the window ring (token t >= s
+//               at s + t mod R), [s+R, C) the top-k set in fill order;
+//   slot pos    [C] int32, -1 when empty;  slot key [C] uint64, the order
+//               key (descending priority, then ascending index);
+//   count, worst slot and worst key of the top-k, two copies each, selected
+//               by the parity of the step (one is read, the other written);
+//   chunk partials of the attention.
+// The ring has one slot more than the window so that within one step the
+// token that leaves the window (d-w) and the token that enters it (d) never
+// share a slot: the row of d-w is read (to copy it into the top-k) while the
+// row of d is written, by different workgroups with no ordering between
+// them.
+//
+// One step is two launches:
+//   decode_step_kernel  one workgroup per (128-slot chunk, b, KV head).
+//                       Every workgroup of (b, h) takes the same insert /
+//                       evict decision from the state, attends over its
+//                       chunk with this step's changes substituted (the
+//                       leaving token masked, the entering token and the new
+//                       token read from their sources), then writes the
+//                       slots of its chunk that change; the chunk-0
+//                       workgroup writes the next step's count and worst key;
+//   decode_combine      merges the chunk partials per query head.  (A merge
+//                       by the last workgroup to finish needs device-scope
+//                       release fences, which write back the whole L2 on
+//                       this chip and cost far more than a second launch.)
 #include "common.h"
 #include "launch.h"
 
 namespace kvpop {
 
-constexpr int DEC_CHUNK = 128;  // slots per attention workgroup
-constexpr int DEC_WAVES = 16;   // waves per attention workgroup
+constexpr int DEC_CHUNK = 128;                   // slots per workgroup
+constexpr int DEC_WAVES = 16;                    // waves per workgroup
 constexpr int DEC_ROWS = DEC_CHUNK / DEC_WAVES;  // slot rows per wave
-constexpr int DEC_MAX_SLOTS = 1 << 20;  // the C-ABI rejects larger caches
-constexpr int DEC_MAX_CHUNKS = DEC_MAX_SLOTS / DEC_CHUNK;  // merge weights held in LDS
+constexpr int DEC_MAX_SLOTS = (1 << 20) + 1;     // the C-ABI allows s + w + k <= 2^20
+constexpr int DEC_MAX_CHUNKS = (DEC_MAX_SLOTS + DEC_CHUNK - 1) / DEC_CHUNK;
 
 __device__ __forceinline__ uint64_t decode_key(float sc, int t) {
   if (sc != sc) sc = -INFINITY;
@@ -40,42 +58,48 @@ __device__ __forceinline__ uint64_t decode_key(float sc, int t) {
   return ((uint64_t)(~ord) << 32) | (uint32_t)t;
 }
 
+static int decode_ring(int w) { return w > 0 ? w + 1 : 0; }
+static int decode_slots(const DecodeShapeInfo &s) { return s.sinks + decode_ring(s.window) + s.topk; }
+
 struct DecodeState {
   void *k, *v;
   int *pos;
   uint64_t *key;
-  int *count;
-  float *part;  // [B*Hq][nchunk][D + 2]
+  int *count;      // [BH][2]
+  int *wslot;      // [BH][2]
+  uint64_t *wkey;  // [BH][2]
+  float *part;     // [B*Hq][nchunk][D + 2]
 };
 
-DecodeState decode_state_view(const DecodeShapeInfo &s, void *base) {
+static DecodeState decode_state_view(const DecodeShapeInfo &s, void *base, size_t *total = nullptr) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t BH = (size_t)s.B * s.Hkv, C = (size_t)s.C;
+  const size_t BH = (size_t)s.B * s.Hkv, C = (size_t)decode_slots(s);
   const size_t es = s.dtype == 0 ? 2 : 4;
-  char *p = reinterpret_cast<char *>(base);
+  const size_t nch = (C + DEC_CHUNK - 1) / DEC_CHUNK;
+  const uintptr_t p = reinterpret_cast<uintptr_t>(base);
   DecodeState st{};
   size_t off = 0;
-  st.k = p + off;
-  off = al(off + BH * C * s.D * es);
-  st.v = p + off;
-  off = al(off + BH * C * s.D * es);
-  st.pos = reinterpret_cast<int *>(p + off);
-  off = al(off + BH * C * 4);
-  st.key = reinterpret_cast<uint64_t *>(p + off);
-  off = al(off + BH * C * 8);
-  st.count = reinterpret_cast<int *>(p + off);
-  off = al(off + BH * 4);
-  st.part = reinterpret_cast<float *>(p + off);
+  auto take = [&](size_t bytes) {
+    void *q = reinterpret_cast<void *>(p + off);
+    off = al(off + bytes);
+    return q;
+  };
+  st.k = take(BH * C * s.D * es);
+  st.v = take(BH * C * s.D * es);
+  st.pos = reinterpret_cast<int *>(take(BH * C * 4));
+  st.key = reinterpret_cast<uint64_t *>(take(BH * C * 8));
+  st.count = reinterpret_cast<int *>(take(BH * 2 * 4));
+  st.wslot = reinterpret_cast<int *>(take(BH * 2 * 4));
+  st.wkey = reinterpret_cast<uint64_t *>(take(BH * 2 * 8));
+  st.part = reinterpret_cast<float *>(take((size_t)s.B * s.Hq * nch * (s.D + 2) * 4));
+  if (total) *total = off;
   return st;
 }
 
 size_t decode_state_bytes(const DecodeShapeInfo &s) {
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t BH = (size_t)s.B * s.Hkv, C = (size_t)s.C;
-  const size_t es = s.dtype == 0 ? 2 : 4;
-  const size_t nch = (C + DEC_CHUNK - 1) / DEC_CHUNK;
-  return 2 * al(BH * C * s.D * es) + al(BH * C * 4) + al(BH * C * 8) + al(BH * 4) +
-         al((size_t)s.B * s.Hq * nch * (s.D + 2) * 4);
+  size_t total = 0;
+  decode_state_view(s, nullptr, &total);
+  return total;
 }
 
 struct DecParams {
@@ -84,7 +108,7 @@ struct DecParams {
   const float *score;
   void *o;
   float *lse;
-  int B, Hq, Hkv, G, D, C, sinks, window, topk, d, nchunk, dtype;
+  int B, Hq, Hkv, G, D, C, R, sinks, window, topk, d, nchunk, dtype;
   float scale_log2;
 };
 
@@ -95,116 +119,21 @@ __global__ void __launch_bounds__(256) decode_init_kernel(DecParams p) {
     p.st.pos[i] = -1;
     p.st.key[i] = ~0ull;
   }
-  if (i < (size_t)p.B * p.Hkv) p.st.count[i] = 0;
-}
-
-template <typename T>
-__device__ __forceinline__ void copy_row(T *dst, const T *src, int D) {
-  for (int e = threadIdx.x; e < D; e += 256) dst[e] = src[e];
-}
-
-// One workgroup per (batch row, KV head): the newly eligible token competes
-// for the top-k, then the new token takes its sink or window slot.
-template <typename T>
-__global__ void __launch_bounds__(256) decode_update(DecParams p) {
-  __shared__ uint64_t red_key[4];
-  __shared__ int red_slot[4];
-  __shared__ int sh_target;
-  const int bh = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = p.sinks, w = p.window, k = p.topk, d = p.d, D = p.D;
-  T *sk = reinterpret_cast<T *>(p.st.k) + (size_t)bh * p.C * D;
-  T *sv = reinterpret_cast<T *>(p.st.v) + (size_t)bh * p.C * D;
-  int *pos = p.st.pos + (size_t)bh * p.C;
-  uint64_t *key = p.st.key + (size_t)bh * p.C;
-  const T *knew = reinterpret_cast<const T *>(p.k) + (size_t)bh * D;
-  const T *vnew = reinterpret_cast<const T *>(p.v) + (size_t)bh * D;
-  const float sc_new = p.score[bh];
-
-  // 1. token e = d - w becomes eligible at this step (with w = 0, the new token)
-  const int e = d - w;
-  if (e >= s && k > 0) {
-    const int src = (w > 0) ? s + e % w : -1;  // its window slot
-    const uint64_t ke = (w > 0) ? key[src] : decode_key(sc_new, d);
-    const int n = p.st.count[bh];
-    if (tid == 0) sh_target = -1;
-    __syncthreads();
-    if (n < k) {
-      if (tid == 0) sh_target = s + w + n;
-    } else {
-      // worst retained top-k slot: the largest key
-      uint64_t best = 0;
-      int bslot = -1;
-      for (int j = tid; j < k; j += 256) {
-        const uint64_t kj = key[s + w + j];
-        if (bslot < 0 || kj > best) {
-          best = kj;
-          bslot = s + w + j;
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t ob = __shfl_xor(best, o);
-        const int os = __shfl_xor(bslot, o);
-        if (os >= 0 && (bslot < 0 || ob > best || (ob == best && os < bslot))) {
-          best = ob;
-          bslot = os;
-        }
-      }
-      if (lane == 0) {
-        red_key[wave] = best;
-        red_slot[wave] = bslot;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint64_t wk = 0;
-        int ws = -1;
-        for (int q = 0; q < 4; ++q)
-          if (red_slot[q] >= 0 && (ws < 0 || red_key[q] > wk)) {
-            wk = red_key[q];
-            ws = red_slot[q];
-          }
-        sh_target = (ws >= 0 && ke < wk) ? ws : -1;
-      }
-    }
-    __syncthreads();
-    const int target = sh_target;
-    if (target >= 0) {
-      if (w > 0) {
-        copy_row(sk + (size_t)target * D, sk + (size_t)src * D, D);
-        copy_row(sv + (size_t)target * D, sv + (size_t)src * D, D);
-      } else {
-        copy_row(sk + (size_t)target * D, knew, D);
-        copy_row(sv + (size_t)target * D, vnew, D);
-      }
-      if (tid == 0) {
-        pos[target] = e;
-        key[target] = ke;
-        if (n < k) p.st.count[bh] = n + 1;
-      }
-    }
-    __syncthreads();  // the window slot is read before the new token overwrites it
-  }
-  // 2. the new token: a sink, or the window ring
-  int slot = -1;
-  if (d < s) slot = d;
-  else if (w > 0) slot = s + d % w;
-  if (slot >= 0) {
-    copy_row(sk + (size_t)slot * D, knew, D);
-    copy_row(sv + (size_t)slot * D, vnew, D);
-    if (tid == 0) {
-      pos[slot] = d;
-      key[slot] = decode_key(sc_new, d);
-    }
+  if (i < (size_t)p.B * p.Hkv * 2) {
+    p.st.count[i] = 0;
+    p.st.wslot[i] = -1;
+    p.st.wkey[i] = 0ull;
   }
 }
 
-// Eight consecutive elements of a slot row, fetched with 16-byte loads.
+// Eight consecutive elements of a slot row, moved with 16-byte accesses.
 template <typename T>
 struct Row8;
 template <>
 struct Row8<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16 *src) { v = *reinterpret_cast<const bf16x8 *>(src); }
+  __device__ __forceinline__ void store(bf16 *dst) const { *reinterpret_cast<bf16x8 *>(dst) = v; }
   __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
 };
 template <>
@@ -213,6 +142,10 @@ struct Row8<float> {
   __device__ __forceinline__ void load(const float *src) {
     a = *reinterpret_cast<const f32x4 *>(src);
     b = *reinterpret_cast<const f32x4 *>(src + 4);
+  }
+  __device__ __forceinline__ void store(float *dst) const {
+    *reinterpret_cast<f32x4 *>(dst) = a;
+    *reinterpret_cast<f32x4 *>(dst + 4) = b;
   }
   __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
@@ -234,11 +167,40 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   return x;
 }
 
+// The decision of step d for one (b, h), the same in every workgroup: the
+// ring slot of the leaving token e = d - w, whether e enters the top-k and
+// where, and the slot of the new token.
+struct DecStep {
+  int e, ring_e;  // leaving token and its ring slot (-1 if none)
+  int n;          // top-k count before the step
+  uint64_t ke;    // order key of e
+  int target;     // top-k slot that receives e (-1: e does not enter)
+  int slot_new;   // slot of the new token d (-1: with w = 0 it only competes)
+};
+
+__device__ __forceinline__ DecStep decode_decide(const DecParams &p, int bh) {
+  DecStep x;
+  const int s = p.sinks, w = p.window, k = p.topk, d = p.d, cur = d & 1;
+  const uint64_t *key = p.st.key + (size_t)bh * p.C;
+  x.e = d - w;
+  const bool compete = k > 0 && x.e >= s;
+  x.ring_e = (w > 0 && x.e >= s) ? s + x.e % p.R : -1;
+  x.n = p.st.count[bh * 2 + cur];
+  x.ke = compete ? (w > 0 ? key[x.ring_e] : decode_key(p.score[bh], d)) : 0ull;
+  x.target = -1;
+  if (compete) {
+    if (x.n < k) x.target = s + p.R + x.n;
+    else if (x.ke < p.st.wkey[bh * 2 + cur]) x.target = p.st.wslot[bh * 2 + cur];
+  }
+  x.slot_new = d < s ? d : (w > 0 ? s + d % p.R : -1);
+  return x;
+}
+
 // Workgroup (chunk, b*Hkv + h): the G query heads of KV head h against slots
-// [chunk*DEC_CHUNK, +DEC_CHUNK).  The kernel is bound by latency, not by
-// bandwidth or arithmetic, so the chunk is spread over DEC_WAVES waves of
-// DEC_ROWS rows each (two or more waves per SIMD), and every wave issues all
-// of its K, V and slot-position loads before it computes anything.  Lane l
+// [chunk*DEC_CHUNK, +DEC_CHUNK) of the state after this step's update.  The
+// attention is bound by latency, not by bandwidth or arithmetic, so the chunk
+// is spread over DEC_WAVES waves of DEC_ROWS rows each, and every wave issues
+// all of its K, V and position loads before it computes anything.  Lane l
 // covers 8 elements at 8*(l % LPR) of a slot row (LPR = D/8 lanes per row,
 // RPW = 64/LPR rows per load instruction).  Phases:
 //   1. logits: per-lane partial dot products finished by a DPP sum over the
@@ -246,42 +208,104 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 //   2. one wave per query head reduces that head's maximum and sum of
 //      exponentials over the chunk;
 //   3. each wave forms its rows' probabilities and partial PV sums, reduced
-//      over the rows of the wave, then over the waves through LDS.
+//      over the rows of the wave, then over the waves through LDS;
+//   4. the slots of this chunk that change in this step are written, and
+//      chunk 0 writes the next step's count and worst retained token.
 // G (query heads per KV head) and D are template parameters so that register
 // arrays are indexed statically and every reduction is unrolled.
 template <typename T, int G, int D>
-__global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
-  constexpr int EPL = 8;                // elements per lane and row
-  constexpr int LPR = D / EPL;          // lanes per row: 16 (D=128) or 8 (D=64)
-  constexpr int RPW = 64 / LPR;         // rows per load instruction: 4 or 8
-  constexpr int NRG = DEC_ROWS / RPW;   // row groups per wave: 2 or 1
+__global__ void __launch_bounds__(DEC_WAVES * 64) decode_step_kernel(DecParams p) {
+  constexpr int EPL = 8;               // elements per lane and row
+  constexpr int LPR = D / EPL;         // lanes per row: 16 (D=128) or 8 (D=64)
+  constexpr int RPW = 64 / LPR;        // rows per load instruction: 4 or 8
+  constexpr int NRG = DEC_ROWS / RPW;  // row groups per wave: 2 or 1
   static_assert(DEC_ROWS % RPW == 0, "whole row groups per wave");
   static_assert(G <= DEC_WAVES, "one wave per query head in phase 2");
   __shared__ float lg[G][DEC_CHUNK];
   __shared__ float ml[G][2];  // per head: maximum (log2 units) and sum
   __shared__ float osum[DEC_WAVES][G][D];
+  __shared__ uint64_t red_key[DEC_WAVES];
+  __shared__ int red_slot[DEC_WAVES];
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r_in = lane / LPR, c = lane % LPR;
-  const T *sk = reinterpret_cast<const T *>(p.st.k) + (size_t)bh * p.C * D;
-  const T *sv = reinterpret_cast<const T *>(p.st.v) + (size_t)bh * p.C * D;
-  const int *pos = p.st.pos + (size_t)bh * p.C;
+  T *sk = reinterpret_cast<T *>(p.st.k) + (size_t)bh * p.C * D;
+  T *sv = reinterpret_cast<T *>(p.st.v) + (size_t)bh * p.C * D;
+  int *pos = p.st.pos + (size_t)bh * p.C;
+  uint64_t *key = p.st.key + (size_t)bh * p.C;
+  const T *knew = reinterpret_cast<const T *>(p.k) + (size_t)bh * D;
+  const T *vnew = reinterpret_cast<const T *>(p.v) + (size_t)bh * D;
   const int j0 = chunk * DEC_CHUNK;
   const int nslots = min(DEC_CHUNK, p.C - j0);
-
-  // every load of this wave, up front; rows past the chunk's end re-read
-  // its last row and are masked
-  Row8<T> kr[NRG], vr[NRG];
+  // Every load of this wave is issued before anything waits on one: the
+  // chunk's slot rows and positions, the two rows a step can substitute (the
+  // leaving token's, from its ring slot, and the new token's), and the
+  // decision's inputs.  The decision then picks, per row, which data is the
+  // slot's after this step.  Rows past the chunk's end re-read its last row
+  // and are masked.
+  const int ring_e = (p.window > 0 && p.d - p.window >= p.sinks) ? p.sinks + (p.d - p.window) % p.R : -1;
+  const T *ek = ring_e >= 0 ? sk + (size_t)ring_e * D : knew;  // source of the token entering the top-k
+  const T *ev = ring_e >= 0 ? sv + (size_t)ring_e * D : vnew;
+  Row8<T> kr[NRG], vr[NRG], ke8, ve8, kn8, vn8;
+  int pj[NRG];
+#pragma unroll
+  for (int i = 0; i < NRG; ++i) {
+    const int j = wave * DEC_ROWS + i * RPW + r_in;
+    const int jj = j0 + min(j, nslots - 1);
+    kr[i].load(sk + (size_t)jj * D + c * EPL);
+    vr[i].load(sv + (size_t)jj * D + c * EPL);
+    pj[i] = pos[jj];
+  }
+  ke8.load(ek + c * EPL);
+  ve8.load(ev + c * EPL);
+  kn8.load(knew + c * EPL);
+  vn8.load(vnew + c * EPL);
+  // chunk 0 keeps the top-k's worst key up to date for the next step.  The
+  // only slot an eviction can empty is the current worst W, so the largest
+  // key of the other slots is all it needs besides the entering key; its
+  // loads go out here with the rest.
+  constexpr int SCAN = 4;  // keys per thread in flight (4096 slots per pass)
+  const int cur = p.d & 1, kb = p.sinks + p.R;
+  const int w_cur = p.st.wslot[bh * 2 + cur];
+  uint64_t ex_best = 0;
+  int ex_slot = -1;
+  auto scan_pass = [&](int base) {
+    uint64_t kk[SCAN];
+#pragma unroll
+    for (int u = 0; u < SCAN; ++u) {
+      const int j = base + tid + u * DEC_WAVES * 64;
+      kk[u] = j < p.topk ? key[kb + j] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < SCAN; ++u) {
+      const int j = base + tid + u * DEC_WAVES * 64;
+      if (j < p.topk && kb + j != w_cur && (ex_slot < 0 || kk[u] > ex_best)) {
+        ex_best = kk[u];
+        ex_slot = kb + j;
+      }
+    }
+  };
+  const bool full_topk = p.topk > 0 && p.st.count[bh * 2 + cur] == p.topk;
+  if (chunk == 0 && full_topk) scan_pass(0);
+  const DecStep x = decode_decide(p, bh);
   bool ok[NRG];
 #pragma unroll
   for (int i = 0; i < NRG; ++i) {
     const int j = wave * DEC_ROWS + i * RPW + r_in;
-    const int jj = min(j, nslots - 1);
-    const size_t off = (size_t)(j0 + jj) * D + c * EPL;
-    kr[i].load(sk + off);
-    vr[i].load(sv + off);
-    ok[i] = j < nslots && pos[j0 + jj] >= 0;
+    const int jj = j0 + min(j, nslots - 1);
+    bool valid = pj[i] >= 0 && jj != x.ring_e;
+    if (jj == x.target) {
+      kr[i] = ke8;
+      vr[i] = ve8;
+      valid = true;
+    }
+    if (jj == x.slot_new) {
+      kr[i] = kn8;
+      vr[i] = vn8;
+      valid = true;
+    }
+    ok[i] = j < nslots && valid;
   }
   float qv[G][EPL];
 #pragma unroll
@@ -298,11 +322,11 @@ __global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
     const int j = wave * DEC_ROWS + i * RPW + r_in;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float x = 0.f;
+      float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x += qv[g][e] * kr[i][e];
-      x = lane_group_sum<LPR>(x);
-      if (c == 0) lg[g][j] = ok[i] ? x * p.scale_log2 : -INFINITY;
+      for (int e = 0; e < EPL; ++e) s += qv[g][e] * kr[i][e];
+      s = lane_group_sum<LPR>(s);
+      if (c == 0) lg[g][j] = ok[i] ? s * p.scale_log2 : -INFINITY;
     }
   }
   __syncthreads();
@@ -340,8 +364,7 @@ __global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
     for (int e = 0; e < EPL; ++e) vf[e] = ok[i] ? vr[i][e] : 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float m = ml[g][0];
-      const float pg = ok[i] ? exp2f(lg[g][j] - m) : 0.f;
+      const float pg = ok[i] ? exp2f(lg[g][j] - ml[g][0]) : 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] += pg * vf[e];
     }
@@ -351,10 +374,10 @@ __global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float x = acc[g][e];
+      float s = acc[g][e];
 #pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) x += __shfl_xor(x, o);
-      acc[g][e] = x;
+      for (int o = LPR; o < 64; o <<= 1) s += __shfl_xor(s, o);
+      acc[g][e] = s;
     }
   if (r_in == 0)
 #pragma unroll
@@ -372,6 +395,77 @@ __global__ void __launch_bounds__(DEC_WAVES * 64) decode_attn(DecParams p) {
     if (e == 0) {
       pp[D] = ml[g][0];
       pp[D + 1] = ml[g][1];
+    }
+  }
+
+  // 4. the slots of this chunk that change; only this workgroup read their
+  // rows above, and the entering token's source row is not written in this
+  // step
+  if (x.target >= j0 && x.target < j0 + nslots) {
+    for (int e0 = tid * EPL; e0 < D; e0 += DEC_WAVES * 64 * EPL) {
+      Row8<T> r;
+      r.load(ek + e0);
+      r.store(sk + (size_t)x.target * D + e0);
+      r.load(ev + e0);
+      r.store(sv + (size_t)x.target * D + e0);
+    }
+    if (tid == 0) {
+      pos[x.target] = x.e;
+      key[x.target] = x.ke;
+    }
+  }
+  if (x.slot_new >= j0 && x.slot_new < j0 + nslots) {
+    for (int e0 = tid * EPL; e0 < D; e0 += DEC_WAVES * 64 * EPL) {
+      Row8<T> r;
+      r.load(knew + e0);
+      r.store(sk + (size_t)x.slot_new * D + e0);
+      r.load(vnew + e0);
+      r.store(sv + (size_t)x.slot_new * D + e0);
+    }
+    if (tid == 0) {
+      pos[x.slot_new] = p.d;
+      key[x.slot_new] = decode_key(p.score[bh], p.d);
+    }
+  }
+  // the next step's count and worst retained token (chunk 0 of (b, h)); no
+  // key read here is written in this step
+  if (chunk == 0) {
+    const int nxt = cur ^ 1;
+    const int k = p.topk;
+    int ws = w_cur;
+    uint64_t wk = p.st.wkey[bh * 2 + cur];
+    if (x.target >= 0 && x.n < k) {  // filling: the worst is the largest key so far
+      if (x.n == 0 || x.ke > wk) {
+        ws = x.target;
+        wk = x.ke;
+      }
+    } else if (x.target >= 0) {  // W was evicted: the larger of the others' maximum and e's key
+      for (int base = SCAN * DEC_WAVES * 64; base < k; base += SCAN * DEC_WAVES * 64) scan_pass(base);
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t ob = __shfl_xor(ex_best, o);
+        const int os = __shfl_xor(ex_slot, o);
+        if (os >= 0 && (ex_slot < 0 || ob > ex_best)) {
+          ex_best = ob;
+          ex_slot = os;
+        }
+      }
+      if (lane == 0) {
+        red_key[wave] = ex_best;
+        red_slot[wave] = ex_slot;
+      }
+      __syncthreads();
+      ws = x.target;
+      wk = x.ke;
+      for (int q = 0; q < DEC_WAVES; ++q)
+        if (red_slot[q] >= 0 && red_key[q] > wk) {
+          wk = red_key[q];
+          ws = red_slot[q];
+        }
+    }
+    if (tid == 0) {
+      p.st.count[bh * 2 + nxt] = x.n + ((x.target >= 0 && x.n < k) ? 1 : 0);
+      p.st.wslot[bh * 2 + nxt] = ws;
+      p.st.wkey[bh * 2 + nxt] = wk;
     }
   }
 }
@@ -428,11 +522,12 @@ static DecParams decode_params(const DecodeShapeInfo &s, void *state) {
   p.Hkv = s.Hkv;
   p.G = s.Hq / s.Hkv;
   p.D = s.D;
-  p.C = s.C;
+  p.R = decode_ring(s.window);
+  p.C = decode_slots(s);
   p.sinks = s.sinks;
   p.window = s.window;
   p.topk = s.topk;
-  p.nchunk = (s.C + DEC_CHUNK - 1) / DEC_CHUNK;
+  p.nchunk = (p.C + DEC_CHUNK - 1) / DEC_CHUNK;
   p.dtype = s.dtype;
   p.scale_log2 = s.scale * kLog2e;
   return p;
@@ -440,37 +535,35 @@ static DecParams decode_params(const DecodeShapeInfo &s, void *state) {
 
 hipError_t launch_decode_init(const DecodeShapeInfo &s, void *state, hipStream_t st) {
   DecParams p = decode_params(s, state);
-  const size_t n = (size_t)s.B * s.Hkv * s.C;
+  const size_t slots = (size_t)p.B * p.Hkv * p.C, books = (size_t)p.B * p.Hkv * 2;
+  const size_t n = slots > books ? slots : books;
   hipLaunchKernelGGL(decode_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static bool launch_attn_g(const DecParams &p, dim3 grid, hipStream_t st) {
+static bool launch_step_g(const DecParams &p, dim3 grid, hipStream_t st) {
+  const dim3 block(DEC_WAVES * 64);
   switch (p.G) {
-    case 1: hipLaunchKernelGGL((decode_attn<T, 1, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 2: hipLaunchKernelGGL((decode_attn<T, 2, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 3: hipLaunchKernelGGL((decode_attn<T, 3, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 4: hipLaunchKernelGGL((decode_attn<T, 4, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 5: hipLaunchKernelGGL((decode_attn<T, 5, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 6: hipLaunchKernelGGL((decode_attn<T, 6, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 7: hipLaunchKernelGGL((decode_attn<T, 7, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
-    case 8: hipLaunchKernelGGL((decode_attn<T, 8, D>), grid, dim3(DEC_WAVES * 64), 0, st, p); return true;
+    case 1: hipLaunchKernelGGL((decode_step_kernel<T, 1, D>), grid, block, 0, st, p); return true;
+    case 2: hipLaunchKernelGGL((decode_step_kernel<T, 2, D>), grid, block, 0, st, p); return true;
+    case 3: hipLaunchKernelGGL((decode_step_kernel<T, 3, D>), grid, block, 0, st, p); return true;
+    case 4: hipLaunchKernelGGL((decode_step_kernel<T, 4, D>), grid, block, 0, st, p); return true;
+    case 5: hipLaunchKernelGGL((decode_step_kernel<T, 5, D>), grid, block, 0, st, p); return true;
+    case 6: hipLaunchKernelGGL((decode_step_kernel<T, 6, D>), grid, block, 0, st, p); return true;
+    case 7: hipLaunchKernelGGL((decode_step_kernel<T, 7, D>), grid, block, 0, st, p); return true;
+    case 8: hipLaunchKernelGGL((decode_step_kernel<T, 8, D>), grid, block, 0, st, p); return true;
     default: return false;
   }
 }
 
 template <typename T>
 static hipError_t run_decode(DecParams &p, hipStream_t st) {
-  hipLaunchKernelGGL(decode_update<T>, dim3(p.B * p.Hkv), dim3(256), 0, st, p);
   const dim3 grid(p.nchunk, p.B * p.Hkv);
-  if (p.D == 128) {
-    if (!launch_attn_g<T, 128>(p, grid, st)) return hipErrorInvalidValue;
-  } else if (p.D == 64) {
-    if (!launch_attn_g<T, 64>(p, grid, st)) return hipErrorInvalidValue;
-  } else {
-    return hipErrorInvalidValue;
-  }
+  const bool ok = p.D == 128 ? launch_step_g<T, 128>(p, grid, st)
+                : p.D == 64  ? launch_step_g<T, 64>(p, grid, st)
+                             : false;
+  if (!ok) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_combine<T>, dim3(p.B * p.Hq), dim3(256), 0, st, p);
   return hipGetLastError();
 }
