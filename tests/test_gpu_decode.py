@@ -36,6 +36,8 @@ CASES = [
     (180, 3, 3, 64, "f32", 1, 8, 25),       # one query head per KV head
     (240, 6, 2, 128, "bf16", 4, 16, 60),    # 3 query heads per KV head
     (1300, 2, 1, 64, "bf16", 4, 64, 1100),  # ten chunks, the last one ragged
+    (300, 2, 1, 64, "bf16", 1, 8, 1),       # one top-k slot: an eviction leaves no other key
+    (250, 4, 2, 128, "bf16", 0, 1, 5),      # one-token window: a ring of two slots
 ]
 
 
