@@ -33,7 +33,7 @@ struct FwdParams {
   const int *cu;
   int n_docs;
   // budget-masked mode
-  const int *lists;     // [B*Hkv][nqb][list_cap] key positions, ascending
+  const int *lists;     // [B*Hkv][nqb][list_cap] key positions (two segments, see budget_lists)
   const int *list_len;       // [B*Hkv][nqb]
   const int *list_len_full;  // [B*Hkv][nqb]: leading entries kept by every query of the block
   const int *rank;      // [B*Hkv][S]
@@ -128,8 +128,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 
   // two stages of (K tile, V tile): one barrier per tile
   __shared__ __align__(16) char smem[2][Tiles::STAGE];
-  __shared__ int kpos_lds[2][KT];
-  __shared__ int krank_lds[2][KT];
+  __shared__ __align__(16) int2 kpr_lds[2][KT];  // per listed key: (position, rank)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
@@ -226,17 +225,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       for (int k = 0; k < LOADS; ++k) {
         const int r = ((wave * LOADS + k) * 64 + lane) / CPR;
         const int idx = tile * KT + r;
-        const int t = (idx < list_len) ? list[idx] : -1;
+        const int raw = list[min(idx, p.list_cap - 1)];  // address independent of list_len
+        const int t = (idx < list_len) ? raw : -1;
         kidx[k] = (t >= 0 && t < p.S) ? t : -1;
       }
       if (tid < KT) {
         const int idx = tile * KT + tid;
-        const int t = (idx < list_len) ? list[idx] : -1;
+        const int raw = list[min(idx, p.list_cap - 1)];
+        const int t = (idx < list_len) ? raw : -1;
         next_kpos = (t >= 0 && t < p.S) ? t : INT32_MAX;
       }
     }
   };
-  auto fetch_sparse = [&](int buf) {
+  auto fetch_sparse = [&](int buf, int tile) {
     if constexpr (SPARSE) {
       const auto kr = make_rsrc(kbase, p.S * ROWB);
       const auto vr = make_rsrc(vbase, p.S * ROWB);
@@ -249,29 +250,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
         lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + ((slot ^ Tiles::vswz(r)) << 4));
       }
       if (tid < KT) {
+        // positions and ranks are read only by masked tiles
         my_kpos = next_kpos;
-        my_krank = my_kpos != INT32_MAX ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
+        my_krank = (tile >= full_tiles && my_kpos != INT32_MAX) ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
       }
     }
   };
   auto store_pos = [&](int buf) {
     if constexpr (SPARSE) {
       if (tid < KT) {
-        kpos_lds[buf][tid] = my_kpos;
-        krank_lds[buf][tid] = my_krank;
+        kpr_lds[buf][tid] = make_int2(my_kpos, my_krank);
       }
     }
   };
 
-  if (n_tiles > 0) {
-    if constexpr (SPARSE) {
-      load_keys(0);
-      fetch_sparse(0);
-      store_pos(0);
-      if (n_tiles > 1) load_keys(1);
-    } else {
-      fetch_dense(0, 0);
+  if constexpr (SPARSE) {
+    // tile 0's list entries are loaded before the list length arrives (their
+    // addresses do not depend on it), so its gathers wait for one round
+    // trip less
+    load_keys(0);
+    if (n_tiles > 0) {
+      fetch_sparse(0, 0);
+      if (0 >= full_tiles) store_pos(0);
+      load_keys(1);
     }
+  } else if (n_tiles > 0) {
+    fetch_dense(0, 0);
   }
   // One tile: wait for its loads, publish them with a barrier (which also
   // retires every read of the other buffer), start the next tile's loads,
@@ -286,7 +290,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
     __syncthreads();
     if (tile + 1 < n_tiles) {
       if constexpr (SPARSE) {
-        fetch_sparse(buf ^ 1);  // key positions loaded during the previous tile
+        fetch_sparse(buf ^ 1, tile + 1);  // key positions loaded during the previous tile
         if (tile + 2 < n_tiles) load_keys(tile + 2);
       } else {
         fetch_dense(tile + 1, buf ^ 1);
@@ -323,20 +327,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = 32 * rb + c_row(i, hf);
-            bool ok;
-            if constexpr (!SPARSE) {
-              const int t = tb + r;
-              ok = qvalid && t <= qpos && t >= qdoc_start;
-            } else {
-              const int t = kpos_lds[buf][r];
-              const int rk = krank_lds[buf][r];
-              ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+          for (int i4 = 0; i4 < 4; ++i4) {
+            // the 4 rows of registers 4*i4 .. 4*i4+3 are adjacent: their
+            // (position, rank) pairs arrive in two 16-byte reads
+            int4 pr[2];
+            if constexpr (SPARSE) {
+              const int r0 = 32 * rb + c_row(4 * i4, hf);
+              pr[0] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0]);
+              pr[1] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0 + 2]);
             }
-            const float x = ok ? s[rb][i] : -INFINITY;
-            s[rb][i] = x;
-            mx = fmaxf(mx, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * i4 + e;
+              bool ok;
+              if constexpr (!SPARSE) {
+                const int t = tb + 32 * rb + c_row(i, hf);
+                ok = qvalid && t <= qpos && t >= qdoc_start;
+              } else {
+                const int t = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
+                const int rk = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
+                ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+              }
+              const float x = ok ? s[rb][i] : -INFINITY;
+              s[rb][i] = x;
+              mx = fmaxf(mx, x);
+            }
           }
         }
       }
@@ -388,7 +403,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       }
     }
     if constexpr (SPARSE) {
-      if (tile + 1 < n_tiles) store_pos(buf ^ 1);
+      if (tile + 1 < n_tiles && tile + 1 >= full_tiles) store_pos(buf ^ 1);
     }
 
   };
