@@ -267,6 +267,7 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build(const WaveletParams
 constexpr int WV_LDS_MAX = 32768;  // eligible tokens per (batch, KV head)
 constexpr int WV_LDS_WORDS = WV_LDS_MAX / 32 + 32;
 
+template <int WV_PER_THREAD>
 __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletParams p) {
   // Thread tid holds elements tid + 1024*j (j < WV_PER_THREAD), so the 64
   // elements of one ballot are consecutive and give two bit words at once.
@@ -275,15 +276,16 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
   // and scatter into a small dummy area, and the bit words are stored by
   // all lanes of a wave (two addresses, consistent data) instead of under a
   // lane test.
-  constexpr int WV_PER_THREAD = WV_LDS_MAX / 1024;
-  __shared__ uint16_t arr[2][WV_LDS_MAX + 64];
+  constexpr int N_MAX = WV_PER_THREAD * 1024;  // eligible tokens this instance holds
+  static_assert(N_MAX <= WV_LDS_MAX, "fits the LDS arrays' budget");
+  __shared__ uint16_t arr[2][N_MAX + 64];
   __shared__ uint32_t wl[WV_LDS_WORDS];
   __shared__ int pl_s[WV_LDS_WORDS];
   __shared__ int sh_waves[16];
   const size_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_e = p.S - p.sinks;
-  if (n_e <= 0 || n_e > WV_LDS_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
+  if (n_e <= 0 || n_e > N_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
   {
     const int *src = p.rank + bh * p.S + p.sinks;
     int r[WV_PER_THREAD];
@@ -347,12 +349,25 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
       const uint32_t word = wl[w];
       const int before = pl_s[w] + __popc(word & below32);
       int pos = ((word >> (lane & 31)) & 1) ? Z + before : i - before;
-      pos = (i < n_e && pos >= 0 && pos < n_e) ? pos : WV_LDS_MAX + lane;
+      pos = (i < n_e && pos >= 0 && pos < n_e) ? pos : N_MAX + lane;
       b[pos] = (uint16_t)(val2[j / 2] >> (16 * (j & 1)));
     }
     __syncthreads();
     cur ^= 1;
   }
+}
+
+// The LDS build when the eligible range fits (16 or 32 elements per thread,
+// whichever holds it), else the global-memory build.
+static void launch_wavelet_build(const WaveletParams &wp, int BH, hipStream_t st) {
+  const int n_e = wp.S - wp.sinks;
+  const bool lds_ok = wp.S <= 65536 && wp.nw1 <= WV_LDS_WORDS;
+  if (lds_ok && n_e <= 16 * 1024)
+    hipLaunchKernelGGL(budget_wavelet_build_lds<16>, dim3(BH), dim3(1024), 0, st, wp);
+  else if (lds_ok && n_e <= WV_LDS_MAX)
+    hipLaunchKernelGGL(budget_wavelet_build_lds<32>, dim3(BH), dim3(1024), 0, st, wp);
+  else
+    hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
 }
 
 // k-th smallest (0-based kk) of the first m eligible ranks (positions
@@ -543,12 +558,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   wp.sinks = sinks;
   wp.L = lo.L;
   wp.nw1 = lo.nw1;
-  if (topk > 0 && s.S - sinks > 0) {
-    if (s.S - sinks <= WV_LDS_MAX && s.S <= 65536 && lo.nw1 <= WV_LDS_WORDS)
-      hipLaunchKernelGGL(budget_wavelet_build_lds, dim3(BH), dim3(1024), 0, st, wp);
-    else
-      hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
-  }
+  if (topk > 0 && s.S - sinks > 0) launch_wavelet_build(wp, BH, st);
   hipLaunchKernelGGL(budget_cutoffs, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, wp, window, topk, cutoff);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -718,12 +728,7 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   wp.sinks = sinks;
   wp.L = lo.L;
   wp.nw1 = lo.nw1;
-  if (topk > 0 && S - sinks > 0) {
-    if (S - sinks <= WV_LDS_MAX && S <= 65536 && lo.nw1 <= WV_LDS_WORDS)
-      hipLaunchKernelGGL(budget_wavelet_build_lds, dim3(BH), dim3(1024), 0, st, wp);
-    else
-      hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
-  }
+  if (topk > 0 && S - sinks > 0) launch_wavelet_build(wp, BH, st);
   tp.rank = rank;
   tp.order = order;
   tp.label = label;
