@@ -200,18 +200,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   // per tensor that write straight into the LDS stage (lane l at +16*l), the
   // swizzles folded into each lane's source offset.  Rows past kend arrive
   // as zeros (they are masked anyway).
-  auto fetch_dense = [&](int tile, int buf) {
-    const int tb = kbeg + tile * KT;
-    const int rows = min(KT, kend - tb);
-    const auto kr = make_rsrc(kbase + (size_t)tb * D, rows * ROWB);
-    const auto vr = make_rsrc(vbase + (size_t)tb * D, rows * ROWB);
+  // Each lane's source offsets within a tile (the swizzles folded in) are
+  // the same for every tile: computed once and kept (opaque to the compiler,
+  // which would otherwise recompute them on every tile).
+  int koff[SPARSE ? 1 : LOADS], voff[SPARSE ? 1 : LOADS];
+  if constexpr (!SPARSE) {
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const int pch = (wave * LOADS + k) * 64 + lane;  // chunk position in the tile
       const int r = pch / CPR, slot = pch % CPR;
-      lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, r * ROWB + ((slot ^ KTile::swz(r)) << 4));
-      lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024,
-                 r * ROWB + ((slot ^ Tiles::vswz(r)) << 4));
+      koff[k] = r * ROWB + ((slot ^ KTile::swz(r)) << 4);
+      voff[k] = r * ROWB + ((slot ^ Tiles::vswz(r)) << 4);
+      asm volatile("" : "+v"(koff[k]), "+v"(voff[k]));
+    }
+  }
+  auto fetch_dense = [&](int tile, int buf) {
+    if constexpr (!SPARSE) {
+      const int tb = kbeg + tile * KT;
+      const int rows = min(KT, kend - tb);
+      const auto kr = make_rsrc(kbase + (size_t)tb * D, rows * ROWB);
+      const auto vr = make_rsrc(vbase + (size_t)tb * D, rows * ROWB);
+#pragma unroll
+      for (int k = 0; k < LOADS; ++k) {
+        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, koff[k]);
+        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, voff[k]);
+      }
     }
   };
 
