@@ -121,7 +121,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   constexpr int NB = D / 32;  // 32-dim blocks of O^T
   constexpr int KT = Tiles::KT;
   constexpr int NRB = KT / 32;  // 32-key row blocks of S^T per tile
-  constexpr int EPC = Tiles::EPC;
   constexpr int CPR = Tiles::CPR;
   constexpr int ROWB = Tiles::ROWB;
   constexpr int LOADS = Tiles::LOADS;

@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) budget_keys(const float *scores, uint64_t
 
 // Bitonic sort of one 2048-key chunk in LDS; 1024 threads, so every stage
 // is one compare-exchange per thread.
-__global__ void __launch_bounds__(1024) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad, int nchunks) {
+__global__ void __launch_bounds__(1024) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad) {
   static_assert(RANK_CH == 2048, "one compare-exchange per thread and stage");
   __shared__ uint64_t sh[RANK_CH];
   const size_t base = (size_t)blockIdx.y * S_pad + (size_t)blockIdx.x * RANK_CH;
@@ -542,7 +542,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   int *cutoff = cutoff_out ? cutoff_out : reinterpret_cast<int *>(w + lo.cutoff);
 
   hipLaunchKernelGGL(budget_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, scores, keys, s.S, lo.S_pad);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad);
   hipLaunchKernelGGL(budget_rank, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, s.S, lo.S_pad, lo.nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -711,7 +711,7 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
   int *order = reinterpret_cast<int *>(w + lo.order);
   hipLaunchKernelGGL(teacher_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, y, lam, delta, keys, S, lo.S_pad, Hkv);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad, lo.nchunks);
+  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad);
   hipLaunchKernelGGL(budget_rank, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, S, lo.S_pad, lo.nchunks);
   hipLaunchKernelGGL(rank_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
   hipError_t e = hipGetLastError();

@@ -76,8 +76,13 @@ __global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, f
   if (i < count) nl[i] = -lse[i] * kLog2e;
 }
 
+// Waves per SIMD the register budget is cut to: three for bf16; the fp32
+// correctness path at D=128 needs more registers and runs two.
+template <typename T, int D>
+constexpr int tgt_waves() { return (sizeof(T) == 2 || D == 64) ? 3 : 2; }
+
 template <typename T, int D, bool SUM_HEADS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) future_target_kernel(const TgtParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_waves<T, D>()))) future_target_kernel(const TgtParams p) {
   using QTile = SwizzledTile<T, D>;
   constexpr int NJ = D / 16;
   constexpr int QT = 64;                                // queries per LDS stage
