@@ -173,3 +173,45 @@ def test_teacher_and_loss_validation():
     assert lib.kvpop_teacher_workspace_size(1, 2, 1000) > 0
     assert lib.kvpop_teacher_workspace_size(0, 2, 1000) == 0
     assert lib.kvpop_boundary_loss_workspace_size(2, 2, 1000) >= 3 * 2 * 2 * 1000 * 4
+
+
+def decode_shape(B=1, Hq=4, Hkv=1, D=128, dtype=kv.BF16, s=4, w=16, k=32):
+    sh = kv.DecodeShape()
+    sh.batch, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.dtype = B, Hq, Hkv, D, dtype
+    sh.softmax_scale = 0.0
+    sh.sinks, sh.window, sh.topk = s, w, k
+    return sh
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=12, Hkv=1), kv.EUNSUPPORTED),        # more than 8 query heads per KV head
+    (dict(Hq=6, Hkv=4), kv.EINVAL),               # not a multiple
+    (dict(D=96), kv.EUNSUPPORTED),
+    (dict(dtype=7), kv.EUNSUPPORTED),
+    (dict(s=0, w=0, k=0), kv.EINVAL),             # no slot at all
+    (dict(s=-1), kv.EINVAL),
+    (dict(k=(1 << 20) + 1), kv.EUNSUPPORTED),     # more than 2^20 slots
+    (dict(B=0), kv.EINVAL),
+])
+def test_decode_validation(kw, status):
+    lib = kv.load()
+    sh = decode_shape(**kw)
+    assert lib.kvpop_decode_state_size(ctypes.byref(sh)) == 0
+    assert lib.kvpop_decode_init(ctypes.byref(sh), FAKE, 1 << 40, None) == status
+
+
+def test_decode_state_size_and_step_errors():
+    lib = kv.load()
+    sh = decode_shape()
+    n = lib.kvpop_decode_state_size(ctypes.byref(sh))
+    # at least the K and V slots: s + (w + 1) + k slots of D bf16 values, per KV head
+    assert n >= 2 * (4 + 17 + 32) * 128 * 2
+    assert lib.kvpop_decode_init(ctypes.byref(sh), FAKE, n - 1, None) == kv.EWORKSPACE
+    assert lib.kvpop_decode_init(ctypes.byref(sh), None, n, None) == kv.EWORKSPACE
+    step = lambda pos, state_bytes, q=FAKE: lib.kvpop_decode_step(ctypes.byref(sh), FAKE, state_bytes, pos, q, FAKE,
+                                                                  FAKE, FAKE, FAKE, FAKE, None)
+    assert step(-1, n) == kv.EINVAL
+    assert step(0, n, q=None) == kv.EINVAL
+    assert step(0, n - 1) == kv.EWORKSPACE
+    if not gpu_available():  # valid arguments reach the device check (never launched on fake pointers)
+        assert step(0, n) == kv.EHIP
