@@ -77,3 +77,32 @@ def test_decode_cache_is_bounded_and_reusable(kvpop_lib):
         r2.append(b.step(*args)[0])
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(r1, r2))
+
+
+def test_decode_at_the_bench_shape(kvpop_lib):
+    """The decode workload bench.py times (batch 1, 32q/8kv, D=128, bf16,
+    budget 4 + 128 + 1916 = 2048), fed 2600 tokens so that the top-k fills at
+    d = 2047 and evicts from then on: every query head's output and LSE at
+    sampled steps (early, around the fill, and the last ones) against the
+    oracle's masked attention row of the same step."""
+    S, Hq, Hkv, D, s, w, kk = 2600, 32, 8, 128, 4, 128, 1916
+    say(f"decode bench shape S={S}")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, "bf16", 4096, device=DEV, heavy_hitters=True, with_scores=True)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    steps = np.array(sorted(set([0, 1, 5, 130, 131, 500, 2046, 2047, 2048, 2049, 2100] + list(range(S - 6, S)))))
+    cache = kvpop_lib.DecodeCache(1, Hq, Hkv, D, q.dtype, s, w, kk)
+    got = {}
+    for d in range(S):
+        o, l = cache.step(q[:, :, d].contiguous(), k[:, :, d].contiguous(), v[:, :, d].contiguous(),
+                          sc[:, :, d].contiguous())
+        if d in steps:
+            got[d] = (o.clone(), l.clone())
+    torch.cuda.synchronize()
+    say("decode bench shape: oracle rows")
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk)
+    ro, rl = budget.masked_attention(dense.to_f64(q), dense.to_f64(k), dense.to_f64(v), r_rank, r_cut, s, w,
+                                     rows=steps)
+    for d in steps:
+        o, l = got[int(d)]
+        assert_lse_close(l, rl[:, :, d], what=f"decode lse step {d}")
+        assert_out_close(o, ro[:, :, d], what=f"decode out step {d}")
