@@ -425,12 +425,15 @@ struct ListParams {
 };
 
 // Key list of query block [d0, d1], in two segments:
-//   full:    the sinks below the window, then the eligible tokens of
-//            [s, d0-w] with rank <= c_{d1}.  Every query of the block keeps
-//            all of them (c_d is non-increasing, so c_{d1} <= c_d), so
-//            their tiles need no per-element mask;
+//   full:    the sinks below the window, the eligible tokens of [s, d0-w]
+//            with rank <= c_{d1}, then the positions (d1-w, d0].  Every query
+//            of the block keeps all of them (c_d is non-increasing, so
+//            c_{d1} <= c_d; and (d1-w, d0] is inside every query's window
+//            and at or before every query), so their tiles need no
+//            per-element mask;
 //   partial: the eligible tokens with c_{d1} < rank <= c_{d0}, then the
-//            window region (d0-w, d1]; these are masked per element.
+//            rest of the window region (d0-w, d1]; these are masked per
+//            element.
 // The size of the full segment is known before the sweep: E_{d1} holds
 // exactly topk tokens of rank <= c_{d1}, so E_{d0} holds topk minus those in
 // (d0-w, d1-w] (at most QB-1 reads).
@@ -467,8 +470,15 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
     __syncthreads();
     n_bfull = p.topk - sh_sub;
   }
-  const int n_full = a_end + n_bfull;
+  // the window region R = (d0-w, d1]: its part (d1-w, d0] lies inside every
+  // query's window and at or before every query of the block, so it joins
+  // the unmasked segment; the rest of R is masked per element
+  const int c_lo = max(0, d0 - p.window + 1);  // first position of R
+  const int wc_lo = max(c_lo, d1 - p.window + 1), wc_hi = d0;  // (d1-w, d0], possibly empty
+  const int n_wc = max(0, wc_hi - wc_lo + 1);
+  const int n_full = a_end + n_bfull + n_wc;
   for (int i = tid; i < a_end && i < p.cap; i += 256) list[i] = i;
+  for (int i = tid; i < n_wc && a_end + n_bfull + i < p.cap; i += 256) list[a_end + n_bfull + i] = wc_lo + i;
   int off_f = a_end, off_p = n_full;
   // sweep length: positions [s, b_hi], or ranks [0, c0]
   const bool by_rank = c0 != CUT_NONE && c0 != CUT_ALL && c0 + 1 < n_e0;
@@ -515,12 +525,16 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
     off_p += tp;
     __syncthreads();
   }
-  const int c_lo = max(0, d0 - p.window + 1);
-  const int n_c = d1 - c_lo + 1;
-  for (int i = tid; i < n_c && off_p + i < p.cap; i += 256) list[off_p + i] = c_lo + i;
+  // the masked part of R: all of R when (d1-w, d0] is empty, else
+  // (d0-w, d1-w] then (d0, d1]
+  const int n_c = d1 - c_lo + 1 - n_wc;
+  for (int i = tid; i < n_c && off_p + i < p.cap; i += 256) {
+    const int t = (n_wc == 0 || c_lo + i < wc_lo) ? c_lo + i : c_lo + i + n_wc;
+    list[off_p + i] = t;
+  }
   if (tid == 0) {
     p.lens[bh * p.nqb + qb] = min(off_p + n_c, p.cap);
-    p.lens_full[bh * p.nqb + qb] = min(off_f, p.cap);
+    p.lens_full[bh * p.nqb + qb] = min(off_f + n_wc, p.cap);
   }
 }
 
