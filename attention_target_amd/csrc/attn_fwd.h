@@ -42,10 +42,10 @@ struct FwdParams {
 };
 
 #ifndef KVPOP_FWD_KT
-#define KVPOP_FWD_KT 64
+#define KVPOP_FWD_KT 32
 #endif
 #ifndef KVPOP_FWD_WAVES
-#define KVPOP_FWD_WAVES 2
+#define KVPOP_FWD_WAVES 3
 #endif
 
 template <typename T, int D>
