@@ -10,7 +10,8 @@
 // Work decomposition
 //  * A block is (batch row, KV head, document, key tile of 256 keys, query
 //    chunk of DT queries).  Its four waves each keep 64 keys of K resident in
-//    registers (the MFMA A operand) for the whole block.
+//    registers (the MFMA A operand) for the whole block; when that grid would
+//    be small (short sequences), blocks of 128 keys, 32 per wave, instead.
 //  * Query tiles of 64 positions stream through double-buffered, swizzled
 //    LDS together with -L_d*log2(e) (precomputed once per call by a small
 //    elementwise kernel).  The tiles are fetched by buffer loads that write
@@ -40,11 +41,12 @@
 
 namespace kvpop {
 
-#ifndef KVPOP_TGT_NCB
-#define KVPOP_TGT_NCB 2
-#endif
-constexpr int TGT_NCB = KVPOP_TGT_NCB;   // 32-key column blocks per wave
-constexpr int TGT_KT = 4 * 32 * TGT_NCB;  // keys per block: 4 waves
+// Keys per wave come in 32-key column blocks (NCB of them): two (256 keys per
+// block) when the grid is large, one (128 keys, twice the blocks) when it
+// would otherwise leave the GPU partly idle.
+constexpr int TGT_SMALL_GRID = 2048;  // blocks below which NCB = 1 is used
+template <int NCB>
+constexpr int tgt_kt() { return 4 * 32 * NCB; }  // keys per block: 4 waves
 
 struct TgtParams {
   const void *q, *k;
@@ -54,19 +56,19 @@ struct TgtParams {
   float scale_log2;
   const int *cu;
   int n_docs;
-  int DT, nch_max, blocks_per_seq, total_blocks, Hp;
+  int DT, nch_max, blocks_per_seq, total_blocks, Hp, kt;
 };
 
 // Number of key tiles of a document of length n that meet query chunk j.
-__host__ __device__ __forceinline__ int tgt_tiles_in_chunk(int n, int j, int DT, int w) {
+__host__ __device__ __forceinline__ int tgt_tiles_in_chunk(int n, int j, int DT, int w, int KT) {
   const int qend = min(n, (j + 1) * DT) - 1;
   if (qend - w < 0) return 0;
-  return min((n + TGT_KT - 1) / TGT_KT, (qend - w) / TGT_KT + 1);
+  return min((n + KT - 1) / KT, (qend - w) / KT + 1);
 }
-__host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w) {
+__host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w, int KT) {
   const int nch = (n + DT - 1) / DT;
   int c = 0;
-  for (int j = 0; j < nch; ++j) c += tgt_tiles_in_chunk(n, j, DT, w);
+  for (int j = 0; j < nch; ++j) c += tgt_tiles_in_chunk(n, j, DT, w, KT);
   return c;
 }
 
@@ -81,8 +83,9 @@ __global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, f
 template <typename T, int D>
 constexpr int tgt_waves() { return (sizeof(T) == 2 || D == 64) ? 3 : 2; }
 
-template <typename T, int D, bool SUM_HEADS>
+template <typename T, int D, bool SUM_HEADS, int NCB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_waves<T, D>()))) future_target_kernel(const TgtParams p) {
+  constexpr int KT = tgt_kt<NCB>();
   using QTile = SwizzledTile<T, D>;
   constexpr int NJ = D / 16;
   constexpr int QT = 64;                                // queries per LDS stage
@@ -108,7 +111,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
       dstart = p.cu[m];
       n = p.cu[m + 1] - dstart;
     }
-    const int cnt = tgt_blocks_in_doc(n, p.DT, p.window);
+    const int cnt = tgt_blocks_in_doc(n, p.DT, p.window, KT);
     if (r < cnt) {
       found = true;
       break;
@@ -120,16 +123,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
   if (nch > p.nch_max) return;
   int j = nch - 1;
   for (; j >= 0; --j) {
-    const int nt = tgt_tiles_in_chunk(n, j, p.DT, p.window);
+    const int nt = tgt_tiles_in_chunk(n, j, p.DT, p.window, KT);
     if (r < nt) break;
     r -= nt;
   }
   if (j < 0) return;
-  const int t0 = r * TGT_KT;  // doc-local first key of the block
+  const int t0 = r * KT;  // doc-local first key of the block
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  constexpr int NCB = TGT_NCB;
   const int tw = t0 + 32 * NCB * wave;  // doc-local first key of this wave
   const int w = p.window;
 
@@ -281,7 +283,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
 struct FinParams {
   const float *part;
   float *out;
-  int B, S, Hq, Hkv, G, window, DT, nch_max, Hp, Hout, agg, mean;
+  int B, S, Hq, Hkv, G, window, DT, nch_max, Hp, Hout, agg, mean, kt;
   float eps;
   const int *cu;
   int n_docs;
@@ -294,7 +296,7 @@ __global__ void __launch_bounds__(256) future_target_finalize(const FinParams p)
   const Doc dd = find_doc(p.cu, p.n_docs, p.S, t);
   const int n = dd.end - dd.start, pos = t - dd.start;
   const int N = max(0, n - pos - p.window);
-  const int fq = (pos / TGT_KT) * TGT_KT + p.window;
+  const int fq = (pos / p.kt) * p.kt + p.window;
   const int nch = (n + p.DT - 1) / p.DT;
   const int jlo = (fq <= n - 1) ? fq / p.DT : nch;
   const float scale = p.mean ? (N > 0 ? 1.f / (float)N : 0.f) : 1.f;
@@ -337,7 +339,10 @@ size_t tgt_workspace_bytes(const ShapeInfo &s) {
 
 template <typename T, int D, bool SUM>
 static hipError_t launch_tgt(const TgtParams &tp, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((future_target_kernel<T, D, SUM>), dim3(grid), dim3(256), 0, st, tp);
+  if (tp.kt == tgt_kt<1>())
+    hipLaunchKernelGGL((future_target_kernel<T, D, SUM, 1>), dim3(grid), dim3(256), 0, st, tp);
+  else
+    hipLaunchKernelGGL((future_target_kernel<T, D, SUM, 2>), dim3(grid), dim3(256), 0, st, tp);
   return hipGetLastError();
 }
 
@@ -361,12 +366,20 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.n_docs = s.n_docs;
   tp.DT = tgt_chunk(s.max_doc);
   tp.nch_max = (s.max_doc + tp.DT - 1) / tp.DT;
-  int per_seq = 0;
-  if (s.cu_host != nullptr) {
-    for (int m = 0; m < s.n_docs; ++m)
-      per_seq += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], tp.DT, window);
-  } else {
-    per_seq = tgt_blocks_in_doc(s.S, tp.DT, window);
+  auto blocks_per_seq = [&](int KT) {
+    int c = 0;
+    if (s.cu_host != nullptr) {
+      for (int m = 0; m < s.n_docs; ++m) c += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], tp.DT, window, KT);
+    } else {
+      c = tgt_blocks_in_doc(s.S, tp.DT, window, KT);
+    }
+    return c;
+  };
+  tp.kt = tgt_kt<2>();
+  int per_seq = blocks_per_seq(tp.kt);
+  if ((long long)per_seq * s.B * s.Hkv < TGT_SMALL_GRID) {
+    tp.kt = tgt_kt<1>();
+    per_seq = blocks_per_seq(tp.kt);
   }
   tp.blocks_per_seq = per_seq;
   tp.total_blocks = per_seq * s.B * s.Hkv;
@@ -396,6 +409,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   fp.G = tp.G;
   fp.window = window;
   fp.DT = tp.DT;
+  fp.kt = tp.kt;
   fp.nch_max = tp.nch_max;
   fp.Hp = tp.Hp;
   fp.Hout = (agg == 2) ? s.Hq : s.Hkv;
