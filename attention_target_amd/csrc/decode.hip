@@ -45,8 +45,10 @@
 namespace kvpop {
 
 constexpr int DEC_CHUNK = 128;                   // slots per workgroup
-constexpr int DEC_WAVES = 16;                    // waves per workgroup
-constexpr int DEC_ROWS = DEC_CHUNK / DEC_WAVES;  // slot rows per wave
+// Waves per workgroup: 16 (8 slot rows each); 8 (16 rows each) for more
+// than 4 query heads per KV head, whose per-head registers would not fit the
+// 128 per lane a 1024-lane workgroup allows.
+__host__ __device__ constexpr int dec_waves(int G) { return G <= 4 ? 16 : 8; }
 constexpr int DEC_MAX_SLOTS = (1 << 20) + 1;     // the C-ABI allows s + w + k <= 2^20
 constexpr int DEC_MAX_CHUNKS = (DEC_MAX_SLOTS + DEC_CHUNK - 1) / DEC_CHUNK;
 
@@ -199,7 +201,7 @@ __device__ __forceinline__ DecStep decode_decide(const DecParams &p, int bh) {
 // Workgroup (chunk, b*Hkv + h): the G query heads of KV head h against slots
 // [chunk*DEC_CHUNK, +DEC_CHUNK) of the state after this step's update.  The
 // attention is bound by latency, not by bandwidth or arithmetic, so the chunk
-// is spread over DEC_WAVES waves of DEC_ROWS rows each, and every wave issues
+// is spread over dec_waves(G) waves of DEC_ROWS rows each, and every wave issues
 // all of its K, V and position loads before it computes anything.  Lane l
 // covers 8 elements at 8*(l % LPR) of a slot row (LPR = D/8 lanes per row,
 // RPW = 64/LPR rows per load instruction).  Phases:
@@ -214,11 +216,13 @@ __device__ __forceinline__ DecStep decode_decide(const DecParams &p, int bh) {
 // G (query heads per KV head) and D are template parameters so that register
 // arrays are indexed statically and every reduction is unrolled.
 template <typename T, int G, int D>
-__global__ void __launch_bounds__(DEC_WAVES * 64) decode_step_kernel(DecParams p) {
+__global__ void __launch_bounds__(dec_waves(G) * 64) decode_step_kernel(DecParams p) {
+  constexpr int DEC_WAVES = dec_waves(G);
+  constexpr int DEC_ROWS = DEC_CHUNK / DEC_WAVES;  // slot rows per wave
   constexpr int EPL = 8;               // elements per lane and row
   constexpr int LPR = D / EPL;         // lanes per row: 16 (D=128) or 8 (D=64)
   constexpr int RPW = 64 / LPR;        // rows per load instruction: 4 or 8
-  constexpr int NRG = DEC_ROWS / RPW;  // row groups per wave: 2 or 1
+  constexpr int NRG = DEC_ROWS / RPW;  // row groups per wave
   static_assert(DEC_ROWS % RPW == 0, "whole row groups per wave");
   static_assert(G <= DEC_WAVES, "one wave per query head in phase 2");
   __shared__ float lg[G][DEC_CHUNK];
@@ -543,7 +547,7 @@ hipError_t launch_decode_init(const DecodeShapeInfo &s, void *state, hipStream_t
 
 template <typename T, int D>
 static bool launch_step_g(const DecParams &p, dim3 grid, hipStream_t st) {
-  const dim3 block(DEC_WAVES * 64);
+  const dim3 block(dec_waves(p.G) * 64);
   switch (p.G) {
     case 1: hipLaunchKernelGGL((decode_step_kernel<T, 1, D>), grid, block, 0, st, p); return true;
     case 2: hipLaunchKernelGGL((decode_step_kernel<T, 2, D>), grid, block, 0, st, p); return true;
