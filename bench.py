@@ -212,14 +212,19 @@ def decode_measurement(kv, dev, steps_fill: int = 2560, steps_timed: int = 200):
             "note": "update + attention + combine launches; the state size does not grow with the sequence"}
 
 
+# The sources that define the two kernels whose HBM counters are committed
+# (the forward and the target pass, their shared helpers and launch glue).
+MEASURED_SOURCES = ("common.h", "launch.h", "attn_fwd.h", "fwd_lse.hip", "future_target.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter readings taken on other sources do not apply."""
+    """Hash of the measured kernels' sources: counter readings taken on other
+    sources do not apply."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in MEASURED_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
