@@ -16,8 +16,9 @@
 // (bf16) is directly the B operand of O^T = V^T P^T.  V stays in its natural
 // row layout in LDS and the V^T operand is gathered with gfx950's transposed
 // LDS reads.  K/V tiles are double-buffered (one barrier per tile), the
-// softmax scale is folded into the exp2 argument, and the running output is
-// rescaled only when a row maximum grows by more than a fixed margin.
+// softmax scale is folded into the exp2 argument, and row maxima are formed
+// only for tiles whose exponentials against the running maximum could exceed
+// a fixed bound (then the running output is rescaled).
 #pragma once
 
 #include "common.h"
@@ -66,9 +67,10 @@ struct FwdTiles {
   __device__ static __forceinline__ int voff(int r, int c) { return r * ROWB + ((c ^ vswz(r)) << 4); }
 };
 
-// Rescaling of the running output is skipped until a row maximum grows by
-// more than this many powers of two; probabilities then stay below 2^TAU.
-constexpr float kLazyRescaleLog2 = 8.f;
+// Bound on the unnormalised probabilities exp2(s*c - m_run) that the
+// running maximum m_run may leave before it is raised (2^8: far from fp32 or
+// bf16 overflow, and a tile's sum of them stays exact enough in fp32).
+constexpr float kProbBound = 256.f;
 
 // A operand of O^T = V^T P^T for the 16-key step j and the 32 head-dim rows
 // of block nb: lane l needs V[keys 16j + 4*hf + {0..3} and 16j + 8 + 4*hf +
@@ -185,6 +187,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   // Running maximum (in log2 units, i.e. already times scale*log2e) and the
   // running sum of this lane half's keys; the halves are added at the end.
   float m_run = -INFINITY, l_run = 0.f;
+  bool started = false;  // every row of the wave has a finite m_run
   const float c = p.scale_log2;
 
   // budget-masked path: the key positions of this lane's rows of the next
@@ -317,61 +320,64 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       const char *kl = smem[buf];
       const char *vl = smem[buf] + Tiles::K_BYTES;
       f32x16 s[NRB];
+      // S^T tile.  z is an opaque zero: it keeps the LDS reads of a second
+      // pass inside that pass (read once for both, they would hold 32 more
+      // registers through the first).
+      auto logits = [&](int z) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        s[rb] = f32x16{};
+        for (int rb = 0; rb < NRB; ++rb) {
+          s[rb] = f32x16{};
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          Frag<T> a;
-          KTile::read(a, kl, 32 * rb + col, 16 * j + 8 * hf);
-          mma(s[rb], a, qf[j]);
+          for (int j = 0; j < NJ; ++j) {
+            Frag<T> a;
+            KTile::read(a, kl + z, 32 * rb + col, 16 * j + 8 * hf);
+            mma(s[rb], a, qf[j]);
+          }
         }
-      }
-
-      // masked row maximum of the raw logits
-      float mx = -INFINITY;
-      if constexpr (FULL) {
+      };
+      // element mask: disallowed logits become -inf
+      auto apply_mask = [&](int z) {
+        if constexpr (!FULL) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              // the 4 rows of registers 4*i4 .. 4*i4+3 are adjacent: their
+              // (position, rank) pairs arrive in two 16-byte reads
+              int4 pr[2];
+              if constexpr (SPARSE) {
+                const int r0 = 32 * rb + c_row(4 * i4, hf) + z;
+                pr[0] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0]);
+                pr[1] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0 + 2]);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                bool ok;
+                if constexpr (!SPARSE) {
+                  const int t = tb + 32 * rb + c_row(i, hf);
+                  ok = qvalid && t <= qpos && t >= qdoc_start;
+                } else {
+                  const int t = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
+                  const int rk = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
+                  ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+                }
+                s[rb][i] = ok ? s[rb][i] : -INFINITY;
+              }
+            }
+          }
+        }
+      };
+      // row maximum over both lane halves, in log2 units
+      auto row_max = [&]() {
+        float mx = -INFINITY;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            // the 4 rows of registers 4*i4 .. 4*i4+3 are adjacent: their
-            // (position, rank) pairs arrive in two 16-byte reads
-            int4 pr[2];
-            if constexpr (SPARSE) {
-              const int r0 = 32 * rb + c_row(4 * i4, hf);
-              pr[0] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0]);
-              pr[1] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0 + 2]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * i4 + e;
-              bool ok;
-              if constexpr (!SPARSE) {
-                const int t = tb + 32 * rb + c_row(i, hf);
-                ok = qvalid && t <= qpos && t >= qdoc_start;
-              } else {
-                const int t = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
-                const int rk = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
-                ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
-              }
-              const float x = ok ? s[rb][i] : -INFINITY;
-              s[rb][i] = x;
-              mx = fmaxf(mx, x);
-            }
-          }
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxc = mx * c;
-      // lazy rescale: only when some row's maximum grew by more than 2^TAU
-      if (__ballot(mxc > m_run + kLazyRescaleLog2) != 0) {
-        const float m_new = fmaxf(m_run, mxc);
+        return fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      };
+      auto rescale_to = [&](float m_new) {
         const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
         if constexpr (WITH_O) {
@@ -379,17 +385,52 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
           for (int nb = 0; nb < NB; ++nb) o_acc[nb] *= alpha;
         }
         m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      };
+      // P^T in place: exponentials against m, summed per lane
+      auto exponentials = [&](float m) {
+        float lt = 0.f;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
+        for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, -m_use));
-          s[rb][i] = pv;
-          l_run += pv;
+          for (int i = 0; i < 16; ++i) {
+            const float pv = fast_exp2(__builtin_fmaf(s[rb][i], c, -m));
+            s[rb][i] = pv;
+            lt += pv;
+          }
         }
+        return lt;
+      };
+
+      // Once every row of the wave has a running maximum, a tile first takes
+      // its exponentials against it directly.  A sum of non-negative terms
+      // bounds each of them, so when every lane's sum stays within the bound
+      // no probability exceeds it and the row maxima are not needed.
+      // Otherwise (a larger or non-finite sum), and while some row has no
+      // maximum yet, the tile is redone against its exact masked maximum,
+      // which also brings the running one to where later tiles pass again.
+      float lt = 0.f;
+      bool exact = !started;
+      if (started) {
+        int z = 0;
+        asm volatile("" : "+s"(z));
+        logits(z);
+        apply_mask(z);
+        lt = exponentials(m_run);
+        exact = __ballot(!(lt <= kProbBound)) != 0;
       }
+      if (exact) {
+        // z differs from the first block's: its LDS reads must not be
+        // merged with those (that would keep 32 more registers live)
+        int z = 0;
+        asm volatile("" : "+s"(z));
+        logits(z);
+        apply_mask(z);
+        const float mxc = row_max();
+        if (__ballot(mxc > m_run) != 0) rescale_to(fmaxf(m_run, mxc));
+        lt = exponentials(m_run == -INFINITY ? 0.f : m_run);
+        started = __ballot(m_run == -INFINITY) == 0;
+      }
+      l_run += lt;
 
       if constexpr (WITH_O) {
 #pragma unroll

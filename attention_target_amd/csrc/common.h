@@ -62,14 +62,6 @@ __device__ __forceinline__ f32x16 mma_add(const Frag<float> &a, const Frag<float
 
 // Multiplies a fragment by x, rounding each element back to the fragment type
 // (round to nearest even for bf16).
-__device__ __forceinline__ void scale_frag(Frag<bf16> &f, float x) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)((float)f.v[e] * x);
-}
-__device__ __forceinline__ void scale_frag(Frag<float> &f, float x) {
-  f.lo *= x;
-  f.hi *= x;
-}
 
 // Eight consecutive elements starting at p (16-byte aligned).
 __device__ __forceinline__ void load_frag(Frag<bf16> &f, const bf16 *p) {

@@ -13,17 +13,19 @@
 //    registers (the MFMA A operand) for the whole block; when that grid would
 //    be small (short sequences), blocks of 128 keys, 32 per wave, instead.
 //  * Query tiles of 64 positions stream through double-buffered, swizzled
-//    LDS together with -L_d*log2(e) (precomputed once per call by a small
+//    LDS together with -L_d/scale (precomputed once per call by a small
 //    elementwise kernel).  The tiles are fetched by buffer loads that write
 //    straight into LDS, with the swizzle folded into each lane's source
 //    offset, so no registers or LDS stores are spent on staging.  For every
-//    query head of the group each wave computes S = Q K'^T (32 queries x 64
-//    keys per half tile) with MFMA.  K' is K
-//    multiplied by scale*log2(e) (rounded to the input type once per block)
-//    and the MFMA addend is -L_d*log2(e), so the accumulator is directly the
-//    exp2 argument: per element only exp2 and one add into the per-lane sum
-//    of the lane's key remain on the VALU.  No running max is needed: with
-//    the dense normaliser s_{d,t} <= L_d.
+//    query head of the group each wave computes S = Q K^T (32 queries x 64
+//    keys per half tile) with MFMA.  The MFMA addend is -L_d/scale, so the
+//    accumulator is q_d.k_t - L_d/scale and the exp2 argument is that times
+//    scale*log2(e): per element a multiply, exp2 and one add into the
+//    per-lane sum of the lane's key remain on the VALU.  (Folding the scale
+//    into K instead would save the multiply, but rounding scale*K to bf16
+//    perturbs each logit by up to 2^-9 of sum_i |q_i k_i| * scale, e.g.
+//    0.04 nats at logits near 30.)  No running max is needed: with the dense
+//    normaliser s_{d,t} <= L_d.
 //  * The masks d >= t + w and "inside the document" are applied only on the
 //    sub-tiles that cross them.
 //  * At the end the two halves of each wave add their sums (one shuffle)
@@ -50,7 +52,7 @@ constexpr int tgt_kt() { return 4 * 32 * NCB; }  // keys per block: 4 waves
 
 struct TgtParams {
   const void *q, *k;
-  const float *nl;  // -L*log2(e) per query, [B, Hq, S]
+  const float *nl;  // -L/scale per query, [B, Hq, S]
   float *part;
   int B, S, Hq, Hkv, G, window;
   float scale_log2;
@@ -72,10 +74,11 @@ __host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w, 
   return c;
 }
 
-// -L*log2(e) for every query: the MFMA addend of the target kernel.
-__global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, float *nl, size_t count) {
+// -L/scale for every query (mul = -1/scale): the MFMA addend of the target
+// kernel, in the units of the raw logits q.k.
+__global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, float *nl, float mul, size_t count) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < count) nl[i] = -lse[i] * kLog2e;
+  if (i < count) nl[i] = lse[i] * mul;
 }
 
 // Waves per SIMD the register budget is cut to: three for bf16; the fp32
@@ -135,11 +138,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
   const int tw = t0 + 32 * NCB * wave;  // doc-local first key of this wave
   const int w = p.window;
 
-  // ---- resident K fragments (B operand), pre-multiplied by scale*log2(e) ----
-  // S = Q K'^T puts queries on the rows (registers) and keys on the columns
-  // (lanes), so every lane accumulates the column sum of one key.  With K'
-  // holding scale*log2(e) and the MFMA addend holding -L_d*log2(e), the
-  // accumulator is already the exp2 argument s_{d,t}*log2(e) - L_d*log2(e).
+  // ---- resident K fragments (B operand) ----
+  // S = Q K^T puts queries on the rows (registers) and keys on the columns
+  // (lanes), so every lane accumulates the column sum of one key.  With the
+  // MFMA addend holding -L_d/scale, the accumulator times scale*log2(e) is
+  // the exp2 argument s_{d,t}*log2(e) - L_d*log2(e).
   const T *kbase = reinterpret_cast<const T *>(p.k) + ((size_t)b * p.Hkv + h) * (size_t)p.S * D;
   Frag<T> kf[NCB][NJ];
 #pragma unroll
@@ -149,7 +152,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       load_frag(kf[cb][jj], kr + 16 * jj);
-      scale_frag(kf[cb][jj], p.scale_log2);
     }
   }
 
@@ -184,7 +186,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
     gg = it / n_st;
     q0 = qs_al + QT * (it % n_st);
   };
-  // Starts the loads of stage `it` (64 rows of one head and their -L*log2e)
+  // Starts the loads of stage `it` (64 rows of one head and their -L/scale)
   // into LDS buffer `buf`.  The buffers end at the document end, so rows past
   // it arrive as zeros; they are masked out below.
   auto fetch = [&](auto bufc, int it) {
@@ -211,8 +213,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
     }
   };
   // One half stage: 32 query rows starting at row `h32` of the stage.
+  const float cs = p.scale_log2;
   auto half = [&](const char *ql, const float *nl, int q0) {
-    // accumulators start at -L*log2(e) of the query row held by each
+    // accumulators start at -L/scale of the query row held by each
     // register (read twice from LDS rather than kept in a third tile)
     f32x16 s[NCB];
 #pragma unroll
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i]);
+        for (int i = 0; i < 16; ++i) acc[cb][i & 1] += fast_exp2(s[cb][i] * cs);
     } else {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
@@ -244,7 +247,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int d = q0 + c_row(i, hf);
-          const float pv = fast_exp2(s[cb][i]);
+          const float pv = fast_exp2(s[cb][i] * cs);
           acc[cb][i & 1] += (d >= t + w && d < n && t < n) ? pv : 0.f;
         }
       }
@@ -327,7 +330,7 @@ int tgt_chunk(int max_doc) {
 }
 
 // Workspace: per-chunk partial sums [B, Hq or Hkv, n_chunks, S], then the
-// scaled normaliser -L*log2(e) [B, Hq, S].
+// normaliser in logit units -L/scale [B, Hq, S].
 static size_t tgt_partial_floats(const ShapeInfo &s) {
   const int DT = tgt_chunk(s.max_doc);
   const size_t nch_max = (size_t)((s.max_doc + DT - 1) / DT);
@@ -388,8 +391,9 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   hipError_t e = hipSuccess;
   if (tp.total_blocks > 0) {
     const size_t count = (size_t)s.B * s.Hq * s.S;
+    const float mul = (float)(-1.0 / (double)s.scale);
     hipLaunchKernelGGL(future_target_neg_lse, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, lse, nl,
-                       count);
+                       mul, count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int grid = 8 * ((tp.total_blocks + 7) / 8);
     if (s.dtype == 0 && s.D == 128) e = sum ? launch_tgt<bf16, 128, true>(tp, grid, st) : launch_tgt<bf16, 128, false>(tp, grid, st);

@@ -131,6 +131,45 @@ def make_qkv(batch: int, seqlen: int, n_q_heads: int, n_kv_heads: int, head_dim:
     return out
 
 
+def make_leveled_qkv(seqlen: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: str,
+                     seed: int, key_level, device="cpu", with_scores: bool = False):
+    """Q and K nearly aligned, with K's magnitude set per position.
+
+    Every query is 1 + 0.05 N(0,1) per element and key t is
+    key_level[t] * (1 + 0.05 N(0,1)) per element, so a logit is close to
+    key_level[t] * head_dim / sqrt(head_dim): the sequence of levels shapes
+    how each row's maximum evolves along the keys.  V is N(0,1).  Batch 1.
+    """
+    dev = torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(int(seed))
+    f32 = torch.float32
+    lvl = torch.as_tensor(key_level, dtype=f32, device=dev).reshape(1, 1, seqlen, 1)
+    q = 1.0 + 0.05 * torch.randn(1, n_q_heads, seqlen, head_dim, generator=g, device=dev, dtype=f32)
+    k = lvl * (1.0 + 0.05 * torch.randn(1, n_kv_heads, seqlen, head_dim, generator=g, device=dev, dtype=f32))
+    v = torch.randn(1, n_kv_heads, seqlen, head_dim, generator=g, device=dev, dtype=f32)
+    out = {"q": _to_dtype(q, dtype), "k": _to_dtype(k, dtype), "v": _to_dtype(v, dtype)}
+    if with_scores:
+        out["scores"] = torch.randn(1, n_kv_heads, seqlen, generator=g, device=dev, dtype=f32)
+    return out
+
+
+def key_levels(kind: str, seqlen: int):
+    """Per-position key levels for make_leveled_qkv (natural-log logits near
+    level * sqrt(head_dim)): 'rising' climbs steadily; 'jumps' steps up twice
+    by more than 100 natural-log units (beyond fp32 exp range); 'falling'
+    decreases; 'negative' keeps every logit near -226 at head_dim 128."""
+    t = torch.arange(seqlen, dtype=torch.float64)
+    if kind == "rising":
+        return 0.02 + t * (3.0 / seqlen)
+    if kind == "jumps":
+        return torch.where(t < seqlen // 3, 0.05, torch.where(t < 2 * seqlen // 3, 10.0, 21.0))
+    if kind == "falling":
+        return 3.0 - t * (3.0 / seqlen)
+    if kind == "negative":
+        return torch.full((seqlen,), -20.0, dtype=torch.float64)
+    raise ValueError(kind)
+
+
 def make_workload(name: str, layer: int = 0, device="cpu", seqlen: Optional[int] = None):
     """Materialise one layer of a named workload.
 

@@ -70,6 +70,17 @@ def test_budget_small(kvpop_lib, S, Hq, Hkv, D, dt, s, w, kk, kind):
     check_budget(kvpop_lib, t["q"], t["k"], t["v"], sc.contiguous(), s, w, kk)
 
 
+@pytest.mark.parametrize("kind", ["rising", "jumps", "negative"])
+def test_budget_running_maximum(kvpop_lib, kind):
+    """The sparse forward on logit sequences that steer its running maximum
+    (see the dense forward's test of the same name)."""
+    S = 1500
+    say(f"budget running maximum: {kind}")
+    t = synth.make_leveled_qkv(S, 4, 1, 128, "bf16", 21, synth.key_levels(kind, S), device=DEV,
+                               with_scores=True)
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], t["scores"], 4, 64, 200)
+
+
 def test_budget_full_causal_equals_dense(kvpop_lib):
     """S <= s + w + k: the budget mask is the full causal mask."""
     t = synth.make_qkv(1, 500, 8, 2, 128, "bf16", 3, device=DEV, with_scores=True)

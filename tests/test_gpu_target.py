@@ -95,6 +95,27 @@ def test_random_shapes(kvpop_lib, S, Hq, Hkv, D, dt, docs, w):
     assert_target_close(tn, refn, what="target none")
 
 
+@pytest.mark.parametrize("kind,docs", [("rising", 1), ("jumps", 1), ("jumps", 3), ("falling", 1),
+                                       ("negative", 1), ("negative", 4)])
+def test_forward_running_maximum(kvpop_lib, kind, docs):
+    """Logit sequences that steer the forward's running maximum: a steady climb
+    (repeated rescaling), two jumps of more than 100 natural-log units (a
+    tile's exponentials against the old maximum overflow to +inf and must be
+    redone), a fall (no rescaling after the first tile) and uniformly very
+    negative logits (exponentials against a zero reference underflow)."""
+    S, Hq, Hkv, D, w = 777, 4, 2, 128, 32
+    say(f"running maximum: {kind} docs={docs}")
+    t = synth.make_leveled_qkv(S, Hq, Hkv, D, "bf16", 5 + docs, synth.key_levels(kind, S), device=DEV)
+    cu = synth.cu_seqlens_from_lengths(synth.doc_lengths(S, docs, 50, 11)) if docs > 1 else None
+    q, k, v = t["q"], t["k"], t["v"]
+    cl = cu.tolist() if cu is not None else None
+    r = oracle_ref(q, k, v, cl, w)
+    o, lse, tg = run_gpu(kvpop_lib, q, k, v, cu, w)
+    assert_lse_close(lse, r["lse"])
+    assert_out_bounded(o, r["out"], r["abs_out"], u=U[str(q.dtype)])
+    assert_target_close(tg, dense.target_from_colmass(r["colmass"], Hkv, cl, w, dense.AGG_SUM))
+
+
 @pytest.mark.parametrize("S,Hq,Hkv,w", [(513, 4, 1, 16), (2048, 8, 2, 64)])
 def test_target_fed_with_oracle_lse(kvpop_lib, S, Hq, Hkv, w):
     """The target kernel alone: it receives the oracle's own LSE (fp32)."""
