@@ -90,21 +90,44 @@ __device__ __forceinline__ int vt_off(int lane, int nb) {
   const int y = ROWB >= 256 ? x : ((x >> 1) & 1);
   return (4 * hf + x) * ROWB + 64 * (nb ^ y) + 32 * grp + 8 * (jj & 3);
 }
-template <int ROWB>
-__device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int off_nb, int j, int, int) {
+template <int ROWB, int OFF>
+__device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int off_nb) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const char *p0 = vl + off_nb + 16 * ROWB * j;
+  const char *p0 = vl + off_nb + OFF;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)p0);
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4 *)(__attribute__((address_space(3))) char *)(size_t)(p0 + 8 * ROWB));
   const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   a.v = __builtin_bit_cast(bf16x8, w);
 }
+// The same two reads written out in asm, with their own wait for LDS.
+// Through the builtin the compiler cannot tell them from the direct-to-LDS
+// loads of the next tile that are still in flight and waits for all of those
+// first (that buffer is never read here).  The budget-masked kernel gathers
+// rows that often miss in L2, so that wait costs it ~9%; the dense kernel's
+// loads mostly hit and there the asm form, which the compiler cannot schedule
+// around, is 2% slower.  `addr` is the LDS address of the piece for keys
+// 0..3 without OFF.
+template <int ROWB, int OFF>
+__device__ __forceinline__ void load_vt_asm(Frag<bf16> &a, unsigned addr) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x4 lo, hi;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(lo), "=v"(hi)
+      : "v"(addr), "i"(OFF), "i"(OFF + 8 * ROWB)
+      : "memory");
+  const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  a.v = __builtin_bit_cast(bf16x8, w);
+}
 // fp32 V (correctness path): eight scalar reads through the swizzle.
 template <int ROWB>
-__device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int, int j, int nb, int lane) {
+__device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int j, int nb, int lane) {
   using Tl = FwdTiles<float, ROWB / 4>;
   const int hf = lane >> 5, d = 32 * nb + (lane & 31);
 #pragma unroll
@@ -190,10 +213,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   bool started = false;  // every row of the wave has a finite m_run
   const float c = p.scale_log2;
 
-  // budget-masked path: the key positions of this lane's rows of the next
-  // tile's gathers (loaded one tile ahead), and of row `tid` for the mask
-  int kidx[SPARSE ? LOADS : 1];
-  int next_kpos = INT32_MAX, my_kpos = INT32_MAX, my_krank = 0;
+  // budget-masked path: the raw list entries of this lane's rows of the next
+  // tile's gathers (loaded one tile ahead), and of row `tid` for the mask.
+  // They are checked only when used, a tile later: checking them on arrival
+  // would wait on the list loads right away, and with them (loads complete
+  // in order) on the gathers issued just before.
+  int kraw[SPARSE ? LOADS : 1];
+  int next_raw = -1, my_kpos = INT32_MAX, my_krank = 0;
   int vt_base[NB];  // per-lane part of the transposed V reads
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) vt_base[nb] = vt_off<ROWB>(lane, nb);
@@ -239,18 +265,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) {
         const int r = ((wave * LOADS + k) * 64 + lane) / CPR;
-        const int idx = tile * KT + r;
-        const int raw = list[min(idx, p.list_cap - 1)];  // address independent of list_len
-        const int t = (idx < list_len) ? raw : -1;
-        kidx[k] = (t >= 0 && t < p.S) ? t : -1;
+        kraw[k] = list[min(tile * KT + r, p.list_cap - 1)];  // address independent of list_len
       }
-      if (tid < KT) {
-        const int idx = tile * KT + tid;
-        const int raw = list[min(idx, p.list_cap - 1)];
-        const int t = (idx < list_len) ? raw : -1;
-        next_kpos = (t >= 0 && t < p.S) ? t : INT32_MAX;
-      }
+      if (tid < KT) next_raw = list[min(tile * KT + tid, p.list_cap - 1)];
     }
+  };
+  // a list entry of tile `tile`, row r: its key position, or -1 past the
+  // list end or out of range
+  auto entry = [&](int raw, int tile, int r) {
+    return (tile * KT + r < list_len && raw >= 0 && raw < p.S) ? raw : -1;
   };
   auto fetch_sparse = [&](int buf, int tile) {
     if constexpr (SPARSE) {
@@ -260,13 +283,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       for (int k = 0; k < LOADS; ++k) {
         const int pch = (wave * LOADS + k) * 64 + lane;
         const int r = pch / CPR, slot = pch % CPR;
-        const int row = kidx[k] >= 0 ? kidx[k] * ROWB : 0x7fff0000;
+        const int t = entry(kraw[k], tile, r);
+        const int row = t >= 0 ? t * ROWB : 0x7fff0000;
         lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + ((slot ^ KTile::swz(r)) << 4));
         lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + ((slot ^ Tiles::vswz(r)) << 4));
       }
       if (tid < KT) {
         // positions and ranks are read only by masked tiles
-        my_kpos = next_kpos;
+        const int t = entry(next_raw, tile, tid);
+        my_kpos = t >= 0 ? t : INT32_MAX;
         my_krank = (tile >= full_tiles && my_kpos != INT32_MAX) ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
       }
     }
@@ -433,8 +458,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       l_run += lt;
 
       if constexpr (WITH_O) {
-#pragma unroll
-        for (int j = 0; j < KT / 16; ++j) {
+        // 16-key steps j as compile-time constants: the V reads take the
+        // step's offset as an immediate
+        static_for<KT / 16>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
           Frag<T> pf;
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -449,10 +476,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             Frag<T> a;
-            load_vt<ROWB>(a, vl, vt_base[nb], j, nb, lane);
+            if constexpr (sizeof(T) == 2 && SPARSE) {
+              load_vt_asm<ROWB, Tiles::K_BYTES + 16 * ROWB * j>(a, (unsigned)(size_t)smem[buf] + vt_base[nb]);
+            } else if constexpr (sizeof(T) == 2) {
+              load_vt<ROWB, 16 * ROWB * j>(a, vl, vt_base[nb]);
+            } else {
+              load_vt<ROWB>(a, vl, j, nb, lane);
+            }
             mma(o_acc[nb], a, pf);
           }
-        }
+        });
       }
     }
     if constexpr (SPARSE) {

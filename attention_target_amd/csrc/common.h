@@ -17,6 +17,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace kvpop {
 
 typedef __bf16 bf16;
@@ -136,6 +139,16 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void *lds, 
 }
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
