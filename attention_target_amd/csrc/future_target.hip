@@ -214,24 +214,91 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
   };
   // One half stage: 32 query rows starting at row `h32` of the stage.
   const float cs = p.scale_log2;
-  auto half = [&](const char *ql, const float *nl, int q0) {
-    // accumulators start at -L/scale of the query row held by each
-    // register (read twice from LDS rather than kept in a third tile)
+  // LDS addresses for the asm reads: this lane's Q chunks and its addend
+  // quarter, relative to buffer 0 / half 0 (the rest is an immediate)
+  unsigned a_abs[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) a_abs[jj] = (unsigned)(size_t)&q_lds[0][0] + a_off[jj];
+  const unsigned nl_abs = (unsigned)(size_t)&nl_lds[0][0] + 16 * hf;
+  auto half = [&](auto bufc, auto hhc, int q0) {
+    constexpr int buf = decltype(bufc)::value, hh = decltype(hhc)::value;
+    const char *ql = q_lds[buf] + 32 * hh * ROWB;
+    const float *nl = nl_lds[buf] + 32 * hh;
     f32x16 s[NCB];
+    if constexpr (sizeof(T) == 2 && NJ % 4 == 0) {
+      // The reads are asm: through ordinary loads the compiler cannot tell
+      // them from the next stage's direct-to-LDS loads in flight and waits
+      // for all of those first.  LDS reads complete in order, so each wait
+      // (tied to the registers it guards) counts the reads issued after.
+      constexpr int QO = buf * QBYTES + 32 * hh * ROWB;
+      constexpr int NO = (buf * QT + 32 * hh) * 4;
+      f32x4 nv[4];
+      Frag<T> a[4];
+      asm volatile(
+          "ds_read_b128 %0, %8 offset:%13\n\t"
+          "ds_read_b128 %1, %8 offset:%14\n\t"
+          "ds_read_b128 %2, %8 offset:%15\n\t"
+          "ds_read_b128 %3, %8 offset:%16\n\t"
+          "ds_read_b128 %4, %9 offset:%17\n\t"
+          "ds_read_b128 %5, %10 offset:%17\n\t"
+          "ds_read_b128 %6, %11 offset:%17\n\t"
+          "ds_read_b128 %7, %12 offset:%17"
+          : "=v"(nv[0]), "=v"(nv[1]), "=v"(nv[2]), "=v"(nv[3]), "=v"(a[0].v), "=v"(a[1].v), "=v"(a[2].v),
+            "=v"(a[3].v)
+          : "v"(nl_abs), "v"(a_abs[0]), "v"(a_abs[1]), "v"(a_abs[2]), "v"(a_abs[3]), "i"(NO), "i"(NO + 32),
+            "i"(NO + 64), "i"(NO + 96), "i"(QO)
+          : "memory");
+      asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(nv[0]), "+v"(nv[1]), "+v"(nv[2]), "+v"(nv[3]));
+      // accumulators start at -L/scale of the query row held by each register
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl[8 * i4 + 4 * hf]);
+        for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[cb][4 * i4 + e] = v4[e];
+          for (int e = 0; e < 4; ++e) s[cb][4 * i4 + e] = nv[i4][e];
+#pragma unroll
+      for (int j4 = 0; j4 < NJ; j4 += 4) {
+        if (j4 > 0) {
+          asm volatile(
+              "ds_read_b128 %0, %4 offset:%8\n\t"
+              "ds_read_b128 %1, %5 offset:%8\n\t"
+              "ds_read_b128 %2, %6 offset:%8\n\t"
+              "ds_read_b128 %3, %7 offset:%8"
+              : "=v"(a[0].v), "=v"(a[1].v), "=v"(a[2].v), "=v"(a[3].v)
+              : "v"(a_abs[j4]), "v"(a_abs[j4 + 1]), "v"(a_abs[j4 + 2]), "v"(a_abs[j4 + 3]), "i"(QO)
+              : "memory");
+        }
+        asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[0].v), "+v"(a[1].v));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          mma(s[cb], a[0], kf[cb][j4]);
+          mma(s[cb], a[1], kf[cb][j4 + 1]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[2].v), "+v"(a[3].v));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          mma(s[cb], a[2], kf[cb][j4 + 2]);
+          mma(s[cb], a[3], kf[cb][j4 + 3]);
+        }
       }
+    } else {
+      // accumulators start at -L/scale of the query row held by each
+      // register (read twice from LDS rather than kept in a third tile)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      Frag<T> a;
-      read_a(a, ql, jj);
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) mma(s[cb], a, kf[cb][jj]);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&nl[8 * i4 + 4 * hf]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[cb][4 * i4 + e] = v4[e];
+        }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        Frag<T> a;
+        read_a(a, ql, jj);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) mma(s[cb], a, kf[cb][jj]);
+      }
     }
     const int tlast = tw + 32 * NCB - 1;
     const bool interior = (q0 >= tlast + w) && (q0 + 31 < n) && (tlast < n);
@@ -264,12 +331,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
 
     int gg, q0;
     q_of(it, gg, q0);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int qh = q0 + 32 * hh;
+    static_for<2>([&](auto hhc) {
+      const int qh = q0 + 32 * decltype(hhc)::value;
       // the half must meet a key of this wave and lie inside the chunk
-      if (qh < cq1 && qh + 31 >= tw + w && tw < n) half(q_lds[buf] + 32 * hh * ROWB, nl_lds[buf] + 32 * hh, qh);
-    }
+      if (qh < cq1 && qh + 31 >= tw + w && tw < n) half(bufc, hhc, qh);
+    });
     if constexpr (!SUM_HEADS) {
       if ((it + 1) % n_st == 0) write_partial(h * p.G + gg);
     }
