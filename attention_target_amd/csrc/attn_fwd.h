@@ -109,7 +109,8 @@ __device__ __forceinline__ void load_vt(Frag<bf16> &a, const char *vl, int off_n
 // rows that often miss in L2, so that wait costs it ~9%; the dense kernel's
 // loads mostly hit and there the asm form, which the compiler cannot schedule
 // around, is 2% slower.  `addr` is the LDS address of the piece for keys
-// 0..3 without OFF.
+// 0..3 without OFF.  The outputs are early-clobber so that neither result
+// register can take the address register the second read still needs.
 template <int ROWB, int OFF>
 __device__ __forceinline__ void load_vt_asm(Frag<bf16> &a, unsigned addr) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -119,7 +120,7 @@ __device__ __forceinline__ void load_vt_asm(Frag<bf16> &a, unsigned addr) {
       "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
       "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(lo), "=v"(hi)
+      : "=&v"(lo), "=&v"(hi)
       : "v"(addr), "i"(OFF), "i"(OFF + 8 * ROWB)
       : "memory");
   const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

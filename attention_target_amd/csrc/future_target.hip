@@ -230,6 +230,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
       // them from the next stage's direct-to-LDS loads in flight and waits
       // for all of those first.  LDS reads complete in order, so each wait
       // (tied to the registers it guards) counts the reads issued after.
+      // Outputs are early-clobber: a block issues several reads, so no result
+      // register may share a register with an address not yet consumed.
       constexpr int QO = buf * QBYTES + 32 * hh * ROWB;
       constexpr int NO = (buf * QT + 32 * hh) * 4;
       f32x4 nv[4];
@@ -243,8 +245,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
           "ds_read_b128 %5, %10 offset:%17\n\t"
           "ds_read_b128 %6, %11 offset:%17\n\t"
           "ds_read_b128 %7, %12 offset:%17"
-          : "=v"(nv[0]), "=v"(nv[1]), "=v"(nv[2]), "=v"(nv[3]), "=v"(a[0].v), "=v"(a[1].v), "=v"(a[2].v),
-            "=v"(a[3].v)
+          : "=&v"(nv[0]), "=&v"(nv[1]), "=&v"(nv[2]), "=&v"(nv[3]), "=&v"(a[0].v), "=&v"(a[1].v), "=&v"(a[2].v),
+            "=&v"(a[3].v)
           : "v"(nl_abs), "v"(a_abs[0]), "v"(a_abs[1]), "v"(a_abs[2]), "v"(a_abs[3]), "i"(NO), "i"(NO + 32),
             "i"(NO + 64), "i"(NO + 96), "i"(QO)
           : "memory");
@@ -264,7 +266,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
               "ds_read_b128 %1, %5 offset:%8\n\t"
               "ds_read_b128 %2, %6 offset:%8\n\t"
               "ds_read_b128 %3, %7 offset:%8"
-              : "=v"(a[0].v), "=v"(a[1].v), "=v"(a[2].v), "=v"(a[3].v)
+              : "=&v"(a[0].v), "=&v"(a[1].v), "=&v"(a[2].v), "=&v"(a[3].v)
               : "v"(a_abs[j4]), "v"(a_abs[j4 + 1]), "v"(a_abs[j4 + 2]), "v"(a_abs[j4 + 3]), "i"(QO)
               : "memory");
         }
