@@ -42,29 +42,34 @@ def causal_pairs(lengths):
     return sum(n * (n + 1) // 2 for n in lengths)
 
 
-def cpu_baseline(q, k, v, window, budget_s: float = 20.0):
-    """Time the fp64 oracle (untuned) on one batch row and one KV-head group
-    (4 query heads, all 16384 queries and keys) of layer 0: dense forward with
-    LSE, column sums and the SUM target for 16384 keys."""
+def cpu_baseline(q, k, v, window, min_s: float = 10.0):
+    """Time the fp64 oracle (untuned) on batch row 0 of layer 0, one KV-head
+    group at a time (its G query heads, all S queries and keys: dense forward
+    with LSE, column sums and the SUM target for S keys), until at least
+    `min_s` seconds of CPU work are done or the row's KV heads run out."""
     import numpy as np
     from oracle import dense
-    G = q.shape[1] // k.shape[1]
-    qs = q[0:1, 0:G].to("cpu")
-    ks = k[0:1, 0:1].to("cpu")
-    vs = v[0:1, 0:1].to("cpu")
-    t0 = time.perf_counter()
-    r = dense.reference(qs, ks, vs, window=window)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(r["lse"]).all()
+    Hkv = k.shape[1]
+    G = q.shape[1] // Hkv
     S = q.shape[2]
+    dt, heads = 0.0, 0
+    while heads < Hkv and dt < min_s:
+        qs = q[0:1, heads * G:(heads + 1) * G].to("cpu")
+        ks = k[0:1, heads:heads + 1].to("cpu")
+        vs = v[0:1, heads:heads + 1].to("cpu")
+        t0 = time.perf_counter()
+        r = dense.reference(qs, ks, vs, window=window)
+        dt += time.perf_counter() - t0
+        assert np.isfinite(r["lse"]).all()
+        heads += 1
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    return {"value": S / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0, batch row 0, KV head 0 with its {G} query heads: fp64 dense forward+LSE "
-                      f"and target for {S} keys at S={S} ({dt:.1f} s)",
+    return {"value": heads * S / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0, batch row 0, KV heads 0..{heads - 1} with their {G} query heads each: fp64 dense "
+                      f"forward+LSE and target for {heads * S} keys at S={S} ({dt:.1f} s)",
             "seconds": dt}
 
 
