@@ -228,10 +228,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
     if constexpr (sizeof(T) == 2 && NJ % 4 == 0) {
       // The reads are asm: through ordinary loads the compiler cannot tell
       // them from the next stage's direct-to-LDS loads in flight and waits
-      // for all of those first.  LDS reads complete in order, so each wait
-      // (tied to the registers it guards) counts the reads issued after.
-      // Outputs are early-clobber: a block issues several reads, so no result
-      // register may share a register with an address not yet consumed.
+      // for all of those first.  Each asm block waits for its own reads
+      // before it ends (its outputs are never in flight outside it): the
+      // first brings the addends and the Q chunks of k-steps 0..3, the second
+      // those of k-steps 4..7 while the first group's MFMAs run.  Outputs are
+      // early-clobber: a block issues several reads, so no result register
+      // may share a register with an address not yet consumed.
       constexpr int QO = buf * QBYTES + 32 * hh * ROWB;
       constexpr int NO = (buf * QT + 32 * hh) * 4;
       f32x4 nv[4];
@@ -244,13 +246,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
           "ds_read_b128 %4, %9 offset:%17\n\t"
           "ds_read_b128 %5, %10 offset:%17\n\t"
           "ds_read_b128 %6, %11 offset:%17\n\t"
-          "ds_read_b128 %7, %12 offset:%17"
+          "ds_read_b128 %7, %12 offset:%17\n\t"
+          "s_waitcnt lgkmcnt(0)"
           : "=&v"(nv[0]), "=&v"(nv[1]), "=&v"(nv[2]), "=&v"(nv[3]), "=&v"(a[0].v), "=&v"(a[1].v), "=&v"(a[2].v),
             "=&v"(a[3].v)
           : "v"(nl_abs), "v"(a_abs[0]), "v"(a_abs[1]), "v"(a_abs[2]), "v"(a_abs[3]), "i"(NO), "i"(NO + 32),
             "i"(NO + 64), "i"(NO + 96), "i"(QO)
           : "memory");
-      asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(nv[0]), "+v"(nv[1]), "+v"(nv[2]), "+v"(nv[3]));
       // accumulators start at -L/scale of the query row held by each register
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -265,23 +267,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
               "ds_read_b128 %0, %4 offset:%8\n\t"
               "ds_read_b128 %1, %5 offset:%8\n\t"
               "ds_read_b128 %2, %6 offset:%8\n\t"
-              "ds_read_b128 %3, %7 offset:%8"
+              "ds_read_b128 %3, %7 offset:%8\n\t"
+              "s_waitcnt lgkmcnt(0)"
               : "=&v"(a[0].v), "=&v"(a[1].v), "=&v"(a[2].v), "=&v"(a[3].v)
               : "v"(a_abs[j4]), "v"(a_abs[j4 + 1]), "v"(a_abs[j4 + 2]), "v"(a_abs[j4 + 3]), "i"(QO)
               : "memory");
         }
-        asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[0].v), "+v"(a[1].v));
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          mma(s[cb], a[0], kf[cb][j4]);
-          mma(s[cb], a[1], kf[cb][j4 + 1]);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[2].v), "+v"(a[3].v));
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          mma(s[cb], a[2], kf[cb][j4 + 2]);
-          mma(s[cb], a[3], kf[cb][j4 + 3]);
-        }
+          for (int jj = 0; jj < 4; ++jj) mma(s[cb], a[jj], kf[cb][j4 + jj]);
       }
     } else {
       // accumulators start at -L/scale of the query row held by each
