@@ -7,7 +7,9 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "launch.h"
@@ -78,6 +80,21 @@ kvpop_status check_shape(const kvpop_shape *sh, kvpop::ShapeInfo &s) {
   return KVPOP_OK;
 }
 
+// Alignment the kernels rely on: tensors read or written in 16-byte vectors
+// (Q, K, V, O, workspaces, decode state) and 4-byte fp32/int32 arrays.  NULL
+// entries are optional outputs and are skipped.
+struct Aligned {
+  const char *name;
+  const void *ptr;
+  size_t bytes;
+};
+kvpop_status check_alignment(std::initializer_list<Aligned> ptrs) {
+  for (const Aligned &a : ptrs)
+    if (a.ptr != nullptr && (reinterpret_cast<uintptr_t>(a.ptr) % a.bytes) != 0)
+      return fail(KVPOP_EINVAL, "%s must be %zu-byte aligned", a.name, a.bytes);
+  return KVPOP_OK;
+}
+
 kvpop_status check_device() {
   int n = 0;
   hipError_t e = hipGetDeviceCount(&n);
@@ -129,6 +146,9 @@ kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const v
   kvpop_status st = check_shape(shape, s);
   if (st != KVPOP_OK) return st;
   if (!q || !k || !v || !lse) return fail(KVPOP_EINVAL, "q, k, v and lse must be non-NULL");
+  if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"v", v, 16}, {"o", o, 16}, {"lse", lse, 4},
+                             {"cu_seqlens", s.cu, 4}})) != KVPOP_OK)
+    return st;
   if (s.dtype == KVPOP_F32 && s.D != 64)
     return fail(KVPOP_EUNSUPPORTED, "the fp32 forward supports head_dim 64 only");
   if ((st = check_device()) != KVPOP_OK) return st;
@@ -142,6 +162,9 @@ kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const 
   kvpop_status st = check_shape(shape, s);
   if (st != KVPOP_OK) return st;
   if (!q || !k || !lse || !target) return fail(KVPOP_EINVAL, "q, k, lse and target must be non-NULL");
+  if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"lse", lse, 4}, {"target", target, 4},
+                             {"cu_seqlens", s.cu, 4}, {"workspace", workspace, 16}})) != KVPOP_OK)
+    return st;
   if (window < 0) return fail(KVPOP_EINVAL, "window must be >= 0 (got %d)", window);
   if (agg != KVPOP_AGG_SUM && agg != KVPOP_AGG_MAX && agg != KVPOP_AGG_NONE)
     return fail(KVPOP_EINVAL, "agg must be KVPOP_AGG_SUM, _MAX or _NONE (got %d)", agg);
@@ -164,6 +187,10 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
   if (st != KVPOP_OK) return st;
   if (!q || !k || !v || !scores || !o || !lse)
     return fail(KVPOP_EINVAL, "q, k, v, scores, o and lse must be non-NULL");
+  if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"v", v, 16}, {"o", o, 16}, {"scores", scores, 4},
+                             {"lse", lse, 4}, {"rank_out", rank_out, 4}, {"cutoff_out", cutoff_out, 4},
+                             {"workspace", workspace, 16}})) != KVPOP_OK)
+    return st;
   if (sinks < 0 || window < 0 || topk < 0)
     return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
   if (s.cu != nullptr) return fail(KVPOP_EUNSUPPORTED, "the budget mask does not support packed sequences");
@@ -207,6 +234,10 @@ kvpop_status kvpop_teacher_labels(int32_t batch, int32_t n_kv_heads, int32_t seq
   kvpop_status st = check_seq(batch, n_kv_heads, seqlen);
   if (st != KVPOP_OK) return st;
   if (!target || !label || !boundary) return fail(KVPOP_EINVAL, "target, label and boundary must be non-NULL");
+  if ((st = check_alignment({{"target", target, 4}, {"decay_lambda", decay_lambda, 4}, {"label", label, 4},
+                             {"boundary", boundary, 4}, {"rank_out", rank_out, 4}, {"brank_out", brank_out, 4},
+                             {"workspace", workspace, 16}})) != KVPOP_OK)
+    return st;
   if (sinks < 0 || window < 0 || topk < 0)
     return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
   if (decay_step < 1) return fail(KVPOP_EINVAL, "decay_step must be >= 1 (got %d)", decay_step);
@@ -228,6 +259,10 @@ kvpop_status kvpop_boundary_loss(int32_t batch, int32_t n_kv_heads, int32_t seql
   if (st != KVPOP_OK) return st;
   if (!pred || !label || !boundary || !loss || !grad)
     return fail(KVPOP_EINVAL, "pred, label, boundary, loss and grad must be non-NULL");
+  if ((st = check_alignment({{"pred", pred, 4}, {"label", label, 4}, {"boundary", boundary, 4},
+                             {"weight", weight, 4}, {"loss", loss, 4}, {"grad", grad, 4},
+                             {"workspace", workspace, 16}})) != KVPOP_OK)
+    return st;
   if (sinks < 0 || window < 0 || topk < 0)
     return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
   if (!(tau > 0.f) || std::isinf(tau)) return fail(KVPOP_EINVAL, "tau must be finite and > 0");
@@ -283,6 +318,7 @@ kvpop_status kvpop_decode_init(const kvpop_decode_shape *shape, void *state, siz
   if (st != KVPOP_OK) return st;
   if (state == nullptr || state_bytes < kvpop::decode_state_bytes(s))
     return fail(KVPOP_EWORKSPACE, "decode state of %zu bytes needed", kvpop::decode_state_bytes(s));
+  if ((st = check_alignment({{"state", state, 16}})) != KVPOP_OK) return st;
   if ((st = check_device()) != KVPOP_OK) return st;
   return from_hip(kvpop::launch_decode_init(s, state, (hipStream_t)hip_stream), "kvpop_decode_init launch");
 }
@@ -298,6 +334,9 @@ kvpop_status kvpop_decode_step(const kvpop_decode_shape *shape, void *state, siz
   if (position < 0) return fail(KVPOP_EINVAL, "position must be >= 0 (got %d)", position);
   if (state == nullptr || state_bytes < kvpop::decode_state_bytes(s))
     return fail(KVPOP_EWORKSPACE, "decode state of %zu bytes needed", kvpop::decode_state_bytes(s));
+  if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"v", v, 16}, {"o", o, 16}, {"score", score, 4},
+                             {"lse", lse, 4}, {"state", state, 16}})) != KVPOP_OK)
+    return st;
   if ((st = check_device()) != KVPOP_OK) return st;
   return from_hip(kvpop::launch_decode_step(s, state, position, q, k, v, score, o, lse, (hipStream_t)hip_stream),
                   "kvpop_decode_step launch");

@@ -23,11 +23,13 @@
  *    1/sqrt(D)).  All logarithms returned are natural logarithms.
  *  - dtype: KVPOP_BF16 (bfloat16 Q/K/V/O, fp32 accumulation) or KVPOP_F32.
  *    head_dim must be 64 or 128.
- *  - Every pointer is device memory owned by the caller, 16-byte aligned,
- *    except cu_seqlens_host (host memory, read synchronously during the
- *    call).  The library allocates nothing; workspace is caller-provided and
- *    sized by kvpop_workspace_size().  The stream is a hipStream_t passed as
- *    void* (NULL = the default stream); work is enqueued asynchronously.
+ *  - Every pointer is device memory owned by the caller, except
+ *    cu_seqlens_host (host memory, read synchronously during the call).
+ *    Q, K, V, O, workspaces and the decode state must be 16-byte aligned,
+ *    every fp32 or int32 array 4-byte aligned (KVPOP_EINVAL otherwise).  The
+ *    library allocates nothing; workspace is caller-provided and sized by
+ *    kvpop_workspace_size().  The stream is a hipStream_t passed as void*
+ *    (NULL = the default stream); work is enqueued asynchronously.
  *  - Errors: arguments are validated on the host before anything is
  *    enqueued; a failed validation returns a non-zero status and leaves the
  *    outputs untouched.  kvpop_last_error() returns a thread-local message

@@ -215,3 +215,36 @@ def test_decode_state_size_and_step_errors():
     assert step(0, n - 1) == kv.EWORKSPACE
     if not gpu_available():  # valid arguments reach the device check (never launched on fake pointers)
         assert step(0, n) == kv.EHIP
+
+
+def test_misaligned_pointers_are_rejected():
+    """Tensors the kernels move in 16-byte vectors (Q, K, V, O, workspaces, the
+    decode state) must be 16-byte aligned and fp32/int32 arrays 4-byte
+    aligned; a violation is EINVAL before any device access."""
+    lib = kv.load()
+    sh, _ = shape()
+    odd, half = FAKE + 4, FAKE + 2  # 4-byte aligned but not 16; 2-byte aligned
+    fwd_call = lambda q=FAKE, o=FAKE, lse=FAKE: lib.kvpop_attn_fwd_lse(ctypes.byref(sh), q, FAKE, FAKE, o, lse, None)
+    assert fwd_call(q=odd) == kv.EINVAL
+    assert "aligned" in kv.last_error()
+    assert fwd_call(o=odd) == kv.EINVAL
+    assert fwd_call(lse=half) == kv.EINVAL
+    assert tgt(sh, ws=odd) == kv.EINVAL
+    assert lib.kvpop_future_target(ctypes.byref(sh), FAKE, FAKE, FAKE, 4, 0, 0, 0.0, half, FAKE, 1 << 40,
+                                   None) == kv.EINVAL
+    assert lib.kvpop_budget_mask_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, half, 4, 8, 16, FAKE, FAKE, None, None,
+                                     FAKE, 1 << 40, None) == kv.EINVAL
+    assert lib.kvpop_budget_mask_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 4, 8, 16, FAKE, FAKE, half, None,
+                                     FAKE, 1 << 40, None) == kv.EINVAL
+    dummy = ctypes.c_void_p(16)
+    assert lib.kvpop_teacher_labels(1, 1, 10, dummy, None, 1, 0, 0, 1, ctypes.c_void_p(18), dummy, None, None,
+                                    dummy, 1 << 20, None) == kv.EINVAL
+    assert lib.kvpop_boundary_loss(1, 1, 10, dummy, dummy, dummy, 0, 0, 1, 1.0, None, dummy, ctypes.c_void_p(18),
+                                   dummy, 1 << 20, None) == kv.EINVAL
+    dsh = decode_shape()
+    n = lib.kvpop_decode_state_size(ctypes.byref(dsh))
+    assert lib.kvpop_decode_init(ctypes.byref(dsh), odd, n, None) == kv.EINVAL
+    assert lib.kvpop_decode_step(ctypes.byref(dsh), FAKE, n, 0, odd, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == kv.EINVAL
+    if not gpu_available():  # 4-byte alignment is enough for fp32 arrays (never launched on fake pointers)
+        assert fwd_call(lse=odd) == kv.EHIP
