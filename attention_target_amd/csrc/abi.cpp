@@ -151,6 +151,8 @@ kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const v
     return st;
   if (s.dtype == KVPOP_F32 && s.D != 64)
     return fail(KVPOP_EUNSUPPORTED, "the fp32 forward supports head_dim 64 only");
+  if (kvpop::fwd_grid_blocks(s) > kvpop::kMaxGridBlocks)
+    return fail(KVPOP_EUNSUPPORTED, "the forward would need %lld workgroups", kvpop::fwd_grid_blocks(s));
   if ((st = check_device()) != KVPOP_OK) return st;
   return from_hip(kvpop::launch_fwd(s, q, k, v, o, lse, (hipStream_t)hip_stream), "kvpop_attn_fwd_lse launch");
 }
@@ -169,6 +171,8 @@ kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const 
   if (agg != KVPOP_AGG_SUM && agg != KVPOP_AGG_MAX && agg != KVPOP_AGG_NONE)
     return fail(KVPOP_EINVAL, "agg must be KVPOP_AGG_SUM, _MAX or _NONE (got %d)", agg);
   if (!(eps >= 0.f) || std::isinf(eps)) return fail(KVPOP_EINVAL, "eps must be finite and >= 0");
+  if (kvpop::tgt_grid_blocks(s, window) > kvpop::kMaxGridBlocks)
+    return fail(KVPOP_EUNSUPPORTED, "the target pass would need %lld workgroups", kvpop::tgt_grid_blocks(s, window));
   const size_t need = kvpop::tgt_workspace_bytes(s);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
@@ -199,6 +203,8 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
   if ((long long)s.S * s.D * (s.dtype == KVPOP_F32 ? 4 : 2) >= (1ll << 31))
     return fail(KVPOP_EUNSUPPORTED, "the budget forward gathers keys with 32-bit offsets: seqlen * head_dim * "
                                     "element size must stay below 2^31 bytes");
+  if (kvpop::fwd_grid_blocks(s) > kvpop::kMaxGridBlocks)
+    return fail(KVPOP_EUNSUPPORTED, "the budget forward would need %lld workgroups", kvpop::fwd_grid_blocks(s));
   const size_t need = kvpop::budget_workspace_bytes(s, sinks, window, topk);
   if (workspace == nullptr || ws_bytes < need)
     return fail(KVPOP_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);

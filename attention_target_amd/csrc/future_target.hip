@@ -412,6 +412,21 @@ static hipError_t launch_tgt(const TgtParams &tp, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+long long tgt_grid_blocks(const ShapeInfo &s, int window) {
+  const int DT = tgt_chunk(s.max_doc);
+  auto count = [&](int KT) {
+    long long c = 0;
+    if (s.cu_host != nullptr) {
+      for (int m = 0; m < s.n_docs; ++m) c += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], DT, window, KT);
+    } else {
+      c = tgt_blocks_in_doc(s.S, DT, window, KT);
+    }
+    return c * s.B * s.Hkv;
+  };
+  const long long big = count(tgt_kt<2>());
+  return big < TGT_SMALL_GRID ? count(tgt_kt<1>()) : big;
+}
+
 hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k, const float *lse,
                                 int window, int agg, int mean, float eps, float *target,
                                 void *ws, hipStream_t st) {
@@ -433,7 +448,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.DT = tgt_chunk(s.max_doc);
   tp.nch_max = (s.max_doc + tp.DT - 1) / tp.DT;
   auto blocks_per_seq = [&](int KT) {
-    int c = 0;
+    long long c = 0;
     if (s.cu_host != nullptr) {
       for (int m = 0; m < s.n_docs; ++m) c += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], tp.DT, window, KT);
     } else {
@@ -442,13 +457,14 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
     return c;
   };
   tp.kt = tgt_kt<2>();
-  int per_seq = blocks_per_seq(tp.kt);
-  if ((long long)per_seq * s.B * s.Hkv < TGT_SMALL_GRID) {
+  long long per_seq = blocks_per_seq(tp.kt);
+  if (per_seq * s.B * s.Hkv < TGT_SMALL_GRID) {
     tp.kt = tgt_kt<1>();
     per_seq = blocks_per_seq(tp.kt);
   }
-  tp.blocks_per_seq = per_seq;
-  tp.total_blocks = per_seq * s.B * s.Hkv;
+  if (per_seq * s.B * s.Hkv > kMaxGridBlocks) return hipErrorInvalidConfiguration;  // rejected by the ABI first
+  tp.blocks_per_seq = (int)per_seq;
+  tp.total_blocks = (int)(per_seq * s.B * s.Hkv);
   const bool sum = (agg == 0);
   tp.Hp = sum ? s.Hkv : s.Hq;
   hipError_t e = hipSuccess;

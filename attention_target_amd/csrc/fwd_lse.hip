@@ -10,6 +10,12 @@ static hipError_t run_fwd(const FwdParams &fp, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+long long fwd_grid_blocks(const ShapeInfo &s) {
+  const int G = s.Hq / s.Hkv, HG = fwd_heads_per_block(G);
+  const long long QB = 32 * (4 / HG);
+  return (s.S + QB - 1) / QB * s.B * s.Hkv * (G / HG);
+}
+
 hipError_t launch_fwd(const ShapeInfo &s, const void *q, const void *k, const void *v, void *o,
                       float *lse, hipStream_t st) {
   FwdParams fp{};

@@ -16,6 +16,14 @@ struct ShapeInfo {
   int max_doc;                  // longest document
 };
 
+// Workgroups a launch may use: grid sizes are ints on the device side.
+constexpr long long kMaxGridBlocks = 2147483647ll - 64;
+
+// Workgroups of the forward (dense and budget-masked) and of the target pass
+// for a validated shape, counted in 64 bits.
+long long fwd_grid_blocks(const ShapeInfo &s);
+long long tgt_grid_blocks(const ShapeInfo &s, int window);
+
 hipError_t launch_fwd(const ShapeInfo &s, const void *q, const void *k, const void *v, void *o,
                       float *lse, hipStream_t st);
 

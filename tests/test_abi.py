@@ -248,3 +248,21 @@ def test_misaligned_pointers_are_rejected():
                                  None) == kv.EINVAL
     if not gpu_available():  # 4-byte alignment is enough for fp32 arrays (never launched on fake pointers)
         assert fwd_call(lse=odd) == kv.EHIP
+
+
+def test_grids_beyond_int_range_are_rejected():
+    """Shapes the validation accepts but whose workgroup count would not fit a
+    32-bit grid return EUNSUPPORTED (counted in 64 bits) instead of launching
+    a wrapped-around grid."""
+    lib = kv.load()
+    # forward: 2^24 / 32 query blocks x 4096 KV heads > 2^31 workgroups
+    sh, _ = shape(S=1 << 24, Hq=16384, Hkv=4096, D=64)
+    assert fwd(sh) == kv.EUNSUPPORTED
+    assert "workgroups" in kv.last_error()
+    # target: one 2^24-token document has ~5.4e8 (key tile, query chunk) blocks per KV head
+    sh, _ = shape(S=1 << 24, Hq=32, Hkv=8, D=128)
+    assert tgt(sh, window=4) == kv.EUNSUPPORTED
+    assert "workgroups" in kv.last_error()
+    if not gpu_available():  # one KV head fits (never launched on fake pointers)
+        sh, _ = shape(S=1 << 24, Hq=4, Hkv=1, D=128)
+        assert tgt(sh, window=4, ws_bytes=1 << 50) == kv.EHIP
