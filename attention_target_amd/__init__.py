@@ -174,6 +174,18 @@ def _stream_ptr(t: torch.Tensor, stream: Optional[torch.cuda.Stream]):
     return s.cuda_stream
 
 
+def _retain(stream: Optional[torch.cuda.Stream], *tensors):
+    """Tensors this binding allocated (on the current stream) and handed to
+    kernels enqueued on another `stream`: marked as used there, so that the
+    caching allocator does not reuse their memory before that stream has
+    passed this point (on the current stream, stream order already does)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def workspace_size(which: int, q: torch.Tensor, k: torch.Tensor, cu_seqlens=None, sinks: int = 0,
                    window: int = 0, topk: int = 0, scale: float = 0.0) -> int:
     lib = load()
@@ -191,17 +203,21 @@ def attn_fwd_lse(q, k, v, cu_seqlens=None, scale: float = 0.0, need_output: bool
     _require("k", k, q.dtype)
     _require("v", v, q.dtype, k.shape)
     B, Hq, S, D = q.shape
+    made = []
     if lse is None:
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+        made.append(lse)
     _require("lse", lse, torch.float32, (B, Hq, S))
     if need_output and out is None:
         out = torch.empty_like(q)
+        made.append(out)
     if out is not None:
         _require("out", out, q.dtype, q.shape)
     packed = _Packed(cu_seqlens, q.device)
     sh = make_shape(q, k, packed, scale)
     _check(lib.kvpop_attn_fwd_lse(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   _dev(out), lse.data_ptr(), _stream_ptr(q, stream)))
+    _retain(stream, packed.dev, *made)
     return out, lse
 
 
@@ -217,17 +233,21 @@ def future_target(q, k, lse, window: int, agg: Union[str, int] = "sum", mean_ove
     Hkv = k.shape[1]
     _require("lse", lse, torch.float32, (B, Hq, S))
     Hout = Hq if a == AGG_NONE else Hkv
+    made = []
     if out is None:
         out = torch.empty(B, Hout, S, dtype=torch.float32, device=q.device)
+        made.append(out)
     _require("out", out, torch.float32, (B, Hout, S))
     packed = _Packed(cu_seqlens, q.device)
     sh = make_shape(q, k, packed, scale)
     need = int(lib.kvpop_workspace_size(CALL_FUTURE_TARGET, ctypes.byref(sh), 0, window, 0))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
     _check(lib.kvpop_future_target(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), lse.data_ptr(), int(window),
                                    a, int(bool(mean_over_queries)), float(eps), out.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), _stream_ptr(q, stream)))
+    _retain(stream, packed.dev, *made)
     return out
 
 
@@ -246,25 +266,31 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     _require("scores", scores, torch.float32, (B, Hkv, S))
+    made = []
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     if lse is None:
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+        made.append(lse)
     _require("out", out, q.dtype, q.shape)
     _require("lse", lse, torch.float32, (B, Hq, S))
     rank = cutoff = None
     if return_rank_cutoff:
         rank = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
         cutoff = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
+        made += [rank, cutoff]
     packed = _Packed(None, q.device)
     sh = make_shape(q, k, packed, scale)
     need = int(lib.kvpop_workspace_size(CALL_BUDGET_MASK_FWD, ctypes.byref(sh), sinks, window, topk))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
     _check(lib.kvpop_budget_mask_fwd(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      scores.data_ptr(), int(sinks), int(window), int(topk), out.data_ptr(),
                                      lse.data_ptr(), _dev(rank), _dev(cutoff), workspace.data_ptr(),
                                      workspace.numel(), _stream_ptr(q, stream)))
+    _retain(stream, *made)
     return out, lse, rank, cutoff
 
 
@@ -290,12 +316,15 @@ def teacher_labels(target: torch.Tensor, sinks: int, window: int, topk: int,
         rank = torch.empty_like(label)
         brank = torch.empty_like(label)
     need = int(lib.kvpop_teacher_workspace_size(B, H, S))
+    made = [label, bnd, rank, brank]
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=target.device)
+        made.append(workspace)
     _check(lib.kvpop_teacher_labels(B, H, S, target.data_ptr(), _dev(decay_lambda), int(decay_step), int(sinks),
                                     int(window), int(topk), label.data_ptr(), bnd.data_ptr(), _dev(rank),
                                     _dev(brank), workspace.data_ptr(), workspace.numel(),
                                     _stream_ptr(target, stream)))
+    _retain(stream, *made)
     return (label, bnd, rank, brank) if return_ranks else (label, bnd)
 
 
@@ -317,12 +346,15 @@ def boundary_loss(pred: torch.Tensor, label: torch.Tensor, boundary: torch.Tenso
     loss = torch.empty_like(pred)
     grad = torch.empty_like(pred)
     need = int(lib.kvpop_boundary_loss_workspace_size(B, H, S))
+    made = [loss, grad]
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pred.device)
+        made.append(workspace)
     _check(lib.kvpop_boundary_loss(B, H, S, pred.data_ptr(), label.data_ptr(), boundary.data_ptr(), int(sinks),
                                    int(window), int(topk), float(tau), _dev(weight), loss.data_ptr(),
                                    grad.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                    _stream_ptr(pred, stream)))
+    _retain(stream, *made)
     return loss, grad
 
 
@@ -350,6 +382,7 @@ class DecodeCache:
         s = stream if stream is not None else torch.cuda.current_stream(self.state.device)
         _check(lib.kvpop_decode_init(ctypes.byref(self.shape), self.state.data_ptr(), self.state.numel(),
                                      s.cuda_stream))
+        _retain(stream, self.state)
 
     def step(self, q, k, v, score, out=None, lse=None, stream: Optional[torch.cuda.Stream] = None):
         """q [B,Hq,D], k, v [B,Hkv,D] (the cache dtype), score [B,Hkv] fp32."""
@@ -359,13 +392,17 @@ class DecodeCache:
         _require("k", k, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
         _require("v", v, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
         _require("score", score, torch.float32, (sh.batch, sh.n_kv_heads))
+        made = []
         if out is None:
             out = torch.empty_like(q)
+            made.append(out)
         if lse is None:
             lse = torch.empty(sh.batch, sh.n_q_heads, dtype=torch.float32, device=q.device)
+            made.append(lse)
         _check(lib.kvpop_decode_step(ctypes.byref(sh), self.state.data_ptr(), self.state.numel(), self.position,
                                      q.data_ptr(), k.data_ptr(), v.data_ptr(), score.data_ptr(), out.data_ptr(),
                                      lse.data_ptr(), _stream_ptr(q, stream)))
+        _retain(stream, *made)
         self.position += 1
         return out, lse
 

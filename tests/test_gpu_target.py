@@ -203,6 +203,22 @@ def test_bitwise_determinism(kvpop_lib):
     torch.testing.assert_close(t1.isneginf(), t2.isneginf())
 
 
+def test_caller_stream_matches_default_stream(kvpop_lib):
+    """Calls enqueued on a stream the caller passes (outputs, workspace and the
+    device copy of cu_seqlens allocated by the binding and retained on that
+    stream) give the default stream's results, bit for bit."""
+    t = synth.make_qkv(1, 1500, 8, 2, 128, "bf16", 12, device=DEV, heavy_hitters=True)
+    cu = torch.tensor([0, 600, 1500], dtype=torch.int32)
+    o0, l0, t0 = run_gpu(kvpop_lib, t["q"], t["k"], t["v"], cu, 32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o1, l1 = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"], cu_seqlens=cu, stream=side)
+    t1 = kvpop_lib.future_target(t["q"], t["k"], l1, 32, cu_seqlens=cu, stream=side)
+    side.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(t0.nan_to_num(0, 0, 0), t1.nan_to_num(0, 0, 0)) and torch.equal(t0.isneginf(), t1.isneginf())
+
+
 def test_invariant_total_mass_at_zero_window(kvpop_lib):
     """Row sums are 1, so with w = 0 the masses of a KV head's group add up
     to G * (number of queries), whatever the inputs."""
