@@ -261,28 +261,40 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build(const WaveletParams
   }
 }
 
-// The same levels built inside LDS when the eligible range fits: the two
-// arrangements (16-bit ranks) and the level's bit words stay on chip, and
-// only the bit words, prefix counts and zero counts go to global memory.
+// The same levels built inside LDS when the eligible range fits, every level
+// by a workgroup of its own.  The arrangement a level partitions is the
+// eligible ranks stably sorted by the bits above the level, the bit just above
+// it most significant: each partition by a bit makes that bit the leading key
+// and keeps the previous order among equals.  So a level's workgroup builds
+// its arrangement directly by an LSD radix sort on 4-bit digits of that key
+// (at most ceil((L-1)/4) passes, against L partitions in sequence), then
+// stores the level's bit words, prefix counts and zero count like the
+// sequential build.  Both arrangements (16-bit ranks) and the digit counts
+// stay in LDS.
 constexpr int WV_LDS_MAX = 32768;  // eligible tokens per (batch, KV head)
 constexpr int WV_LDS_WORDS = WV_LDS_MAX / 32 + 32;
 
 template <int WV_PER_THREAD>
-__global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletParams p) {
-  // Thread tid holds elements tid + 1024*j (j < WV_PER_THREAD), so the 64
-  // elements of one ballot are consecutive and give two bit words at once.
-  // The level body is straight-line code: a thread's values are read
-  // together and kept two per register, slots past n_e take part with bit 0
-  // and scatter into a small dummy area, and the bit words are stored by
-  // all lanes of a wave (two addresses, consistent data) instead of under a
-  // lane test.
+__global__ void __launch_bounds__(1024) budget_wavelet_levels(const WaveletParams p) {
+  // Thread tid holds elements tid + 1024*j (j < WV_PER_THREAD): the 64
+  // elements of one wave and j form a group of consecutive indices, and the
+  // groups run in index order j-major, then wave.  A radix pass ranks each
+  // element within its group by matching its digit across the group's
+  // ballots (kept, with the digit, two elements per register), counts each
+  // digit per group, scans the counts digit-major and scatters.  Slots past
+  // n_e take the largest digit, so (the sort being stable and they being
+  // last) they stay past n_e.
   constexpr int N_MAX = WV_PER_THREAD * 1024;  // eligible tokens this instance holds
+  constexpr int NG = WV_PER_THREAD * 16;       // groups of 64
+  constexpr int CS = NG + 2;                   // digit row stride: one group's 16 digits hit 16 banks
+  constexpr int NCNT = 16 * CS;
   static_assert(N_MAX <= WV_LDS_MAX, "fits the LDS arrays' budget");
   __shared__ uint16_t arr[2][N_MAX + 64];
+  __shared__ __align__(16) uint16_t cnt[NCNT + 8];
   __shared__ uint32_t wl[WV_LDS_WORDS];
-  __shared__ int pl_s[WV_LDS_WORDS];
   __shared__ int sh_waves[16];
-  const size_t bh = blockIdx.x;
+  const int lvl = (int)blockIdx.x % p.L;
+  const size_t bh = blockIdx.x / p.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_e = p.S - p.sinks;
   if (n_e <= 0 || n_e > N_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
@@ -296,76 +308,111 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build_lds(const WaveletPa
   }
   for (int w = 32 * WV_PER_THREAD + tid; w < p.nw1; w += 1024) wl[w] = 0u;  // words past the ballots' reach
   __syncthreads();
-  const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int nb = p.L - 1 - lvl;  // key bits: bit L-1-kp of a rank is key bit kp
   int cur = 0;
-  for (int lvl = p.L - 1; lvl >= 0; --lvl) {
+  for (int pass = 0; 4 * pass < nb; ++pass) {
     const uint16_t *a = arr[cur];
     uint16_t *b = arr[cur ^ 1];
-    uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
-    int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
-    // An opaque copy of the thread index: element indices are then formed in
-    // place each level rather than kept live across the level loop.
-    int t = tid;
-    asm volatile("" : "+v"(t));
-    // values two per register
-    uint32_t val2[WV_PER_THREAD / 2];
-#pragma unroll
-    for (int j = 0; j < WV_PER_THREAD; j += 2)
-      val2[j / 2] = (uint32_t)a[t + 1024 * j] | ((uint32_t)a[t + 1024 * (j + 1)] << 16);
+    for (int e = tid; e < (NCNT + 8) / 2; e += 1024) reinterpret_cast<uint32_t *>(cnt)[e] = 0u;
+    __syncthreads();
+    // per element: digit (4 bits) and rank among the group's equal digits
+    // (6 bits), two elements per register
+    uint32_t dr[WV_PER_THREAD / 2];
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      const uint32_t v = (val2[j / 2] >> (16 * (j & 1))) & 0xffffu;
-      const int bit = (t + 1024 * j < n_e) ? (int)(v >> lvl) & 1 : 0;
-      const uint64_t m = __ballot(bit);
-      wl[32 * j + 2 * wave + (lane & 1)] = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+      // groups of eight reads: the compiler barrier keeps it from hoisting
+      // all of them (with the packed ranks they would exceed 128 registers)
+      if (j % 8 == 0) asm volatile("" ::: "memory");
+      const uint32_t v = a[tid + 1024 * j];
+      int d = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kp = 4 * pass + q;
+        if (kp < nb) d |= (int)((v >> (p.L - 1 - kp)) & 1u) << q;
+      }
+      d = (tid + 1024 * j < n_e) ? d : 15;
+      uint64_t m = ~0ull;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t bq = __ballot((d >> q) & 1);
+        m &= ((d >> q) & 1) ? bq : ~bq;
+      }
+      const int rk = __popcll(m & below);
+      if (rk == 0) cnt[d * CS + 16 * j + wave] = (uint16_t)__popcll(m);  // the digit's lowest lane
+      const uint32_t e = (uint32_t)(d | (rk << 4));
+      dr[j / 2] = (j & 1) ? (dr[j / 2] | (e << 16)) : e;
     }
     __syncthreads();
+    // exclusive scan of the counts, digit-major (a row's two pad entries are 0)
+    constexpr int PER = (NCNT + 1023) / 1024;
     int local = 0;
-    for (int q = 0; q < wpt; ++q) {
-      const int w = tid * wpt + q;
-      if (w < p.nw1) local += __popc(wl[w]);
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid * PER + e;
+      local += idx < NCNT ? cnt[idx] : 0;
     }
-    int ones;
-    int run = block_excl_scan_1024(local, sh_waves, ones);
-    for (int q = 0; q < wpt; ++q) {
-      const int w = tid * wpt + q;
-      if (w < p.nw1) {
-        pl_s[w] = run;
-        pl[w] = run;
-        bl[w] = wl[w];
-        run += __popc(wl[w]);
+    int total;
+    int run = block_excl_scan_1024(local, sh_waves, total);
+    for (int e = 0; e < PER; ++e) {  // each thread rewrites only its own entries
+      const int idx = tid * PER + e;
+      if (idx < NCNT) {
+        const int c = cnt[idx];
+        cnt[idx] = (uint16_t)run;
+        run += c;
       }
     }
-    const int Z = n_e - ones;
-    if (tid == 0) p.zeros[bh * p.L + lvl] = Z;
     __syncthreads();
-    // stable partition: zeros first, then ones; the count of ones before an
-    // element comes from its bit word (one broadcast read per half wave)
-    const uint32_t below32 = (1u << (lane & 31)) - 1u;
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      const int i = t + 1024 * j;
-      const int w = 32 * j + 2 * wave + (lane >> 5);  // == i >> 5
-      const uint32_t word = wl[w];
-      const int before = pl_s[w] + __popc(word & below32);
-      int pos = ((word >> (lane & 31)) & 1) ? Z + before : i - before;
-      pos = (i < n_e && pos >= 0 && pos < n_e) ? pos : N_MAX + lane;
-      b[pos] = (uint16_t)(val2[j / 2] >> (16 * (j & 1)));
+      if (j % 8 == 0) asm volatile("" ::: "memory");
+      const uint32_t e = (dr[j / 2] >> (16 * (j & 1))) & 0xffffu;
+      const int d = (int)(e & 15u), rk = (int)(e >> 4);
+      const int pos = (int)cnt[d * CS + 16 * j + wave] + rk;
+      b[pos < N_MAX ? pos : N_MAX + lane] = a[tid + 1024 * j];
     }
     __syncthreads();
     cur ^= 1;
   }
+  // this level's bits of the arrangement, prefix counts and zero count
+  const uint16_t *a = arr[cur];
+  uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+  int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+#pragma unroll
+  for (int j = 0; j < WV_PER_THREAD; ++j) {
+    const int i = tid + 1024 * j;
+    const int bit = (i < n_e) ? (int)(a[i] >> lvl) & 1 : 0;
+    const uint64_t m = __ballot(bit);
+    wl[32 * j + 2 * wave + (lane & 1)] = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+  }
+  __syncthreads();
+  const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
+  int local = 0;
+  for (int q = 0; q < wpt; ++q) {
+    const int w = tid * wpt + q;
+    if (w < p.nw1) local += __popc(wl[w]);
+  }
+  int ones;
+  int run = block_excl_scan_1024(local, sh_waves, ones);
+  for (int q = 0; q < wpt; ++q) {
+    const int w = tid * wpt + q;
+    if (w < p.nw1) {
+      pl[w] = run;
+      bl[w] = wl[w];
+      run += __popc(wl[w]);
+    }
+  }
+  if (tid == 0) p.zeros[bh * p.L + lvl] = n_e - ones;
 }
 
-// The LDS build when the eligible range fits (16 or 32 elements per thread,
-// whichever holds it), else the global-memory build.
+// The per-level LDS build when the eligible range fits (16 or 32 elements per
+// thread, whichever holds it), else the sequential global-memory build.
 static void launch_wavelet_build(const WaveletParams &wp, int BH, hipStream_t st) {
   const int n_e = wp.S - wp.sinks;
   const bool lds_ok = wp.S <= 65536 && wp.nw1 <= WV_LDS_WORDS;
   if (lds_ok && n_e <= 16 * 1024)
-    hipLaunchKernelGGL(budget_wavelet_build_lds<16>, dim3(BH), dim3(1024), 0, st, wp);
+    hipLaunchKernelGGL(budget_wavelet_levels<16>, dim3(BH * wp.L), dim3(1024), 0, st, wp);
   else if (lds_ok && n_e <= WV_LDS_MAX)
-    hipLaunchKernelGGL(budget_wavelet_build_lds<32>, dim3(BH), dim3(1024), 0, st, wp);
+    hipLaunchKernelGGL(budget_wavelet_levels<32>, dim3(BH * wp.L), dim3(1024), 0, st, wp);
   else
     hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
 }
