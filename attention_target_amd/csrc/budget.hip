@@ -530,18 +530,30 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   // sweep length: positions [s, b_hi], or ranks [0, c0]
   const bool by_rank = c0 != CUT_NONE && c0 != CUT_ALL && c0 + 1 < n_e0;
   const int n_sweep = c0 == CUT_NONE ? 0 : (by_rank ? c0 + 1 : n_e0);
-  for (int base = 0; base < n_sweep; base += 256) {
-    const int x = base + tid;
-    int t = -1, r = INT32_MAX;
-    if (x < n_sweep) {
-      if (by_rank) {
-        r = x;
-        t = ord[x];
-      } else {
-        t = p.sinks + x;
-        r = rk[t];
+  // the loads of up to LIST_PF chunks of 256 go out before the first chunk
+  // is used (one memory round trip per LIST_PF chunks, not per chunk)
+  constexpr int LIST_PF = 8;
+  for (int base0 = 0; base0 < n_sweep; base0 += 256 * LIST_PF) {
+    int tv[LIST_PF], rv[LIST_PF];
+#pragma unroll
+    for (int u = 0; u < LIST_PF; ++u) {
+      const int x = base0 + 256 * u + tid;
+      tv[u] = -1;
+      rv[u] = INT32_MAX;
+      if (x < n_sweep) {
+        if (by_rank) {
+          rv[u] = x;
+          tv[u] = ord[x];
+        } else {
+          tv[u] = p.sinks + x;
+          rv[u] = rk[tv[u]];
+        }
       }
     }
+#pragma unroll
+    for (int u = 0; u < LIST_PF; ++u) {
+    if (base0 + 256 * u >= n_sweep) break;  // uniform over the workgroup
+    const int t = tv[u], r = rv[u];
     const bool elig = t >= p.sinks && t <= b_hi;
     const bool ff = elig && r <= c1;
     const bool fp = elig && r > c1 && r <= c0;
@@ -571,6 +583,7 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
     off_f += tf;
     off_p += tp;
     __syncthreads();
+    }
   }
   // the masked part of R: all of R when (d1-w, d0] is empty, else
   // (d0-w, d1-w] then (d0, d1]
