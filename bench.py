@@ -76,8 +76,9 @@ def cpu_baseline(q, k, v, window, min_s: float = 10.0):
 def budget_measurement(kv, synth, dev, reps: int = 10):
     """Auxiliary (not part of `value`): the fixed-budget sparse forward on the
     S=32768 budget workload (sinks 4, window 128, top-k 1916 -> B = 2048):
-    rank/cutoff construction, key lists and the masked attention, timed per
-    call with HIP events on the launch stream."""
+    rank/cutoff construction, key lists and the masked attention: `reps`
+    calls back to back (the stream kept busy, as in a training step) between
+    two HIP events on the launch stream, after three warm-up calls."""
     t = synth.make_workload("budget32k", device=dev)
     q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
     s_, w_, k_ = t["sinks"], t["window"], t["topk"]
@@ -88,23 +89,22 @@ def budget_measurement(kv, synth, dev, reps: int = 10):
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    times = []
-    for i in range(reps + 3):
-        e0.record(stream)
-        kv.budget_mask_fwd(q, k, v, sc, s_, w_, k_, return_rank_cutoff=False, out=o, lse=lse, workspace=ws,
-                           stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if i >= 3:
-            times.append(e0.elapsed_time(e1))
-    times.sort()
-    ms = times[len(times) // 2]
+    call = lambda: kv.budget_mask_fwd(q, k, v, sc, s_, w_, k_, return_rank_cutoff=False, out=o, lse=lse,
+                                      workspace=ws, stream=stream)
+    for _ in range(3):
+        call()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
     budget = s_ + w_ + k_
     kept = sum(min(d + 1, budget) for d in range(S))          # kept (query, key) pairs per query head
     flop = 4 * D * Hq * B_ * kept
     return {"workload": f"budget32k: B={B_}, S={S}, {Hq}q/{k.shape[1]}kv heads, head_dim {D}, bf16; "
                         f"sinks {s_}, window {w_}, top-k {k_} (budget {budget})",
-            "ms_per_call_median": round(ms, 4), "sparse_flop_per_call": flop,
+            "ms_per_call": round(ms, 4), "calls_timed": reps, "sparse_flop_per_call": flop,
             "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "whole call (ranks, cutoffs, lists, masked attention); flops count kept pairs only"}
@@ -129,19 +129,19 @@ def paper_pipeline_measurement(kv, q, k, v, window: int, reps: int = 5):
     wst = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, q, k, window=window), dtype=torch.uint8,
                       device=q.device)
     stream = torch.cuda.current_stream(q.device)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    fwd_ms, tgt_ms = [], []
+    # iterations back to back (events between the calls, one synchronisation
+    # at the end), the first two untimed
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
     for i in range(reps + 2):
-        ev[0].record(stream)
+        ev[i][0].record(stream)
         kv.budget_mask_fwd(q, k, v, scores, sinks, window, topk, return_rank_cutoff=False, out=o, lse=lse,
                            workspace=wsb, stream=stream)
-        ev[1].record(stream)
+        ev[i][1].record(stream)
         kv.future_target(q, k, lse, window, out=tgt, workspace=wst, stream=stream)
-        ev[2].record(stream)
-        torch.cuda.synchronize()
-        if i >= 2:
-            fwd_ms.append(ev[0].elapsed_time(ev[1]))
-            tgt_ms.append(ev[1].elapsed_time(ev[2]))
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev[2:]]
+    tgt_ms = [e[1].elapsed_time(e[2]) for e in ev[2:]]
     fwd_ms.sort()
     tgt_ms.sort()
     f, t_ = fwd_ms[len(fwd_ms) // 2], tgt_ms[len(tgt_ms) // 2]
@@ -163,18 +163,20 @@ def teacher_measurement(kv, tgt, window: int, reps: int = 10):
     pred = torch.randn(B_, H, S, generator=g, device=tgt.device, dtype=torch.float32)
     y = torch.where(torch.isfinite(tgt), tgt, torch.full_like(tgt, -30.0)).contiguous()
     stream = torch.cuda.current_stream(tgt.device)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    t_ms, l_ms = [], []
+    # iterations back to back (events between the calls, one synchronisation
+    # at the end), the first two untimed
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
+    keep = []  # outputs stay alive until the stream has run
     for i in range(reps + 2):
-        ev[0].record(stream)
+        ev[i][0].record(stream)
         lab, bnd = kv.teacher_labels(y, sinks, window, topk, decay_lambda=lam, decay_step=16, stream=stream)
-        ev[1].record(stream)
-        kv.boundary_loss(pred, lab, bnd, sinks, window, topk, 1.0, stream=stream)
-        ev[2].record(stream)
-        torch.cuda.synchronize()
-        if i >= 2:
-            t_ms.append(ev[0].elapsed_time(ev[1]))
-            l_ms.append(ev[1].elapsed_time(ev[2]))
+        ev[i][1].record(stream)
+        keep.append(kv.boundary_loss(pred, lab, bnd, sinks, window, topk, 1.0, stream=stream))
+        keep.append((lab, bnd))
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_ms = [e[0].elapsed_time(e[1]) for e in ev[2:]]
+    l_ms = [e[1].elapsed_time(e[2]) for e in ev[2:]]
     t_ms.sort()
     l_ms.sort()
     return {"workload": f"target of one layer of the metric workload [{B_}, {H}, {S}], budget {sinks}+{window}+"
