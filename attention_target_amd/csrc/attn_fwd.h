@@ -261,20 +261,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   // taken from the list (positions loaded a tile earlier by load_keys).
   // Rows past the list end get an offset beyond the buffer and arrive as
   // zeros.  The buffers span the whole (batch, KV head) sequence.
+  // Per-lane constants of the gathers: the row of the tile each load serves
+  // and the swizzled chunk offsets of K and V in that row (the compiler keeps
+  // or recomputes them as registers allow).
+  int g_r[SPARSE ? LOADS : 1], g_ko[SPARSE ? LOADS : 1], g_vo[SPARSE ? LOADS : 1];
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int pch = (wave * LOADS + k) * 64 + lane;
+      const int r = pch / CPR, slot = pch % CPR;
+      g_r[k] = r;
+      g_ko[k] = (slot ^ KTile::swz(r)) << 4;
+      g_vo[k] = (slot ^ Tiles::vswz(r)) << 4;
+    }
+  }
+  // The list entries of a tile come through a buffer resource over the
+  // block's list (entries past list_cap read as zero; every entry at or past
+  // list_len is rejected by entry() below).  The whole offset is in the
+  // per-lane register: the resource's range check does not cover the scalar
+  // offset.
   auto load_keys = [&](int tile) {
     if constexpr (SPARSE) {
+      const auto lr = make_rsrc(list, p.list_cap * 4);
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) {
-        const int r = ((wave * LOADS + k) * 64 + lane) / CPR;
-        kraw[k] = list[min(tile * KT + r, p.list_cap - 1)];  // address independent of list_len
-      }
-      if (tid < KT) next_raw = list[min(tile * KT + tid, p.list_cap - 1)];
+      for (int k = 0; k < LOADS; ++k)
+        kraw[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + g_r[k]) * 4, 0, 0);
+      if (tid < KT) next_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + tid) * 4, 0, 0);
     }
   };
   // a list entry of tile `tile`, row r: its key position, or -1 past the
   // list end or out of range
   auto entry = [&](int raw, int tile, int r) {
-    return (tile * KT + r < list_len && raw >= 0 && raw < p.S) ? raw : -1;
+    const int lim = max(list_len - tile * KT, 0);  // rows of this tile inside the list
+    return ((unsigned)r < (unsigned)lim && (unsigned)raw < (unsigned)p.S) ? raw : -1;
   };
   auto fetch_sparse = [&](int buf, int tile) {
     if constexpr (SPARSE) {
@@ -282,12 +301,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       const auto vr = make_rsrc(vbase, p.S * ROWB);
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) {
-        const int pch = (wave * LOADS + k) * 64 + lane;
-        const int r = pch / CPR, slot = pch % CPR;
-        const int t = entry(kraw[k], tile, r);
+        const int t = entry(kraw[k], tile, g_r[k]);
         const int row = t >= 0 ? t * ROWB : 0x7fff0000;
-        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + ((slot ^ KTile::swz(r)) << 4));
-        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + ((slot ^ Tiles::vswz(r)) << 4));
+        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
+        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
       }
       if (tid < KT) {
         // positions and ranks are read only by masked tiles
