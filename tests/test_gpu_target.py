@@ -130,6 +130,22 @@ def test_target_fed_with_oracle_lse(kvpop_lib, S, Hq, Hkv, w):
     assert_target_close(tg, ref)
 
 
+def test_target_fp32_head_dim_128(kvpop_lib):
+    """fp32 Q and K at head_dim 128 (the forward supports fp32 at head_dim 64
+    only, so the oracle's LSE feeds the target kernel), two ragged documents:
+    the SUM and per-head targets against the oracle."""
+    t = synth.make_qkv(1, 700, 4, 2, 128, "f32", 31, device=DEV)
+    q, k = t["q"], t["k"]
+    cu = torch.tensor([0, 300, 700], dtype=torch.int32)
+    r = oracle_ref(q, k, None, cu.tolist(), 17, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    for agg, code in (("sum", dense.AGG_SUM), ("none", dense.AGG_NONE)):
+        tg = kvpop_lib.future_target(q, k, lse, 17, agg=agg, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        ref = dense.target_from_colmass(r["colmass"], 2, cu.tolist(), 17, code)
+        assert_target_close(tg, ref, what=f"target fp32 D=128 {agg}")
+
+
 def test_qwen4k_full(kvpop_lib):
     """S=4096, 32q/8kv, D=128, bf16, 1% heavy hitters, w=64: every head."""
     t = to_dev(synth.make_workload("qwen4k", device=DEV))
