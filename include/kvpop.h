@@ -22,7 +22,9 @@
  *  - Logit s_{d,t} = softmax_scale * q_d . k_t (softmax_scale <= 0 selects
  *    1/sqrt(D)).  All logarithms returned are natural logarithms.
  *  - dtype: KVPOP_BF16 (bfloat16 Q/K/V/O, fp32 accumulation) or KVPOP_F32.
- *    head_dim must be 64 or 128.
+ *    head_dim must be 64 or 128, except that kvpop_attn_fwd_lse and
+ *    kvpop_budget_mask_fwd take fp32 inputs at head_dim 64 only
+ *    (KVPOP_EUNSUPPORTED otherwise).
  *  - Every pointer is device memory owned by the caller, except
  *    cu_seqlens_host (host memory, read synchronously during the call).
  *    Q, K, V, O, workspaces and the decode state must be 16-byte aligned,

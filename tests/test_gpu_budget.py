@@ -81,6 +81,16 @@ def test_budget_running_maximum(kvpop_lib, kind):
     check_budget(kvpop_lib, t["q"], t["k"], t["v"], t["scores"], 4, 64, 200)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_budget_batch_of_sequences(kvpop_lib, dt):
+    """Three batch rows in one call: each row's ranks and cutoffs come from its
+    own scores, and its output from its own keys."""
+    say(f"budget batch B=3 {dt}")
+    D = 128 if dt == "bf16" else 64    # the fp32 budget forward takes head_dim 64 only
+    t = synth.make_qkv(3, 900, 8, 2, D, dt, 55, device=DEV, with_scores=True)
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], t["scores"], 4, 32, 120)
+
+
 def test_budget_full_causal_equals_dense(kvpop_lib):
     """S <= s + w + k: the budget mask is the full causal mask."""
     t = synth.make_qkv(1, 500, 8, 2, 128, "bf16", 3, device=DEV, with_scores=True)

@@ -38,6 +38,7 @@ CASES = [
     (1300, 2, 1, 64, "bf16", 4, 64, 1100),  # ten chunks, the last one ragged
     (300, 2, 1, 64, "bf16", 1, 8, 1),       # one top-k slot: an eviction leaves no other key
     (250, 4, 2, 128, "bf16", 0, 1, 5),      # one-token window: a ring of two slots
+    (600, 8, 2, 128, "f32", 4, 32, 150),    # fp32 at head_dim 128, several chunks
 ]
 
 
@@ -47,6 +48,30 @@ def test_decode_matches_masked_attention(kvpop_lib, S, Hq, Hkv, D, dt, s, w, kk)
     t = synth.make_qkv(1, S, Hq, Hkv, D, dt, 900 + S, device=DEV, heavy_hitters=True, with_scores=True)
     q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
     cache = kvpop_lib.DecodeCache(1, Hq, Hkv, D, q.dtype, s, w, kk)
+    outs, lses = [], []
+    for d in range(S):
+        o, l = cache.step(q[:, :, d].contiguous(), k[:, :, d].contiguous(), v[:, :, d].contiguous(),
+                          sc[:, :, d].contiguous())
+        outs.append(o)
+        lses.append(l)
+    o = torch.stack(outs, dim=2)
+    l = torch.stack(lses, dim=2)
+    torch.cuda.synchronize()
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk)
+    ro, rl = budget.masked_attention(dense.to_f64(q), dense.to_f64(k), dense.to_f64(v), r_rank, r_cut, s, w)
+    assert_lse_close(l, rl, what="decode lse")
+    assert_out_close(o, ro, what="decode out")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_batch_of_sequences(kvpop_lib, dt):
+    """Three sequences decoded side by side in one cache: each keeps its own
+    budget state, so every sequence matches its own masked attention."""
+    Bn, S, Hq, Hkv, D, s, w, kk = 3, 500, 8, 2, 128, 2, 24, 90
+    say(f"decode batch B={Bn} S={S} {dt}")
+    t = synth.make_qkv(Bn, S, Hq, Hkv, D, dt, 77, device=DEV, heavy_hitters=True, with_scores=True)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    cache = kvpop_lib.DecodeCache(Bn, Hq, Hkv, D, q.dtype, s, w, kk)
     outs, lses = [], []
     for d in range(S):
         o, l = cache.step(q[:, :, d].contiguous(), k[:, :, d].contiguous(), v[:, :, d].contiguous(),
