@@ -261,6 +261,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling runs only: finish with a plain device copy of this many MiB, the "
                          "reference reading for the FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--budget-only", type=int, default=0, metavar="CALLS",
+                    help="profiling runs only: time CALLS calls of the S=32768 budget workload and print "
+                         "that measurement alone (not the metric line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no collectives: "
@@ -274,6 +277,9 @@ def main():
     import synth
     kv.load()
     dev = torch.device("cuda:0")
+    if args.budget_only > 0:
+        print(json.dumps({"budget_path": budget_measurement(kv, synth, dev, reps=args.budget_only)}), flush=True)
+        return
     spec = synth.WORKLOADS["stack36"]
     L, B, S, Hq, Hkv, D, w = spec.layers, spec.batch, spec.seqlen, spec.n_q_heads, spec.n_kv_heads, \
         spec.head_dim, spec.window
