@@ -27,7 +27,7 @@
 // them.
 //
 // One step is two launches:
-//   decode_step_kernel  one workgroup per (128-slot chunk, b, KV head).
+//   decode_step_kernel  one workgroup per (64-slot chunk, b, KV head).
 //                       Every workgroup of (b, h) takes the same insert /
 //                       evict decision from the state, attends over its
 //                       chunk with this step's changes substituted (the
@@ -44,11 +44,12 @@
 
 namespace kvpop {
 
-constexpr int DEC_CHUNK = 128;                   // slots per workgroup
-// Waves per workgroup: 16 (8 slot rows each); 8 (16 rows each) for more
-// than 4 query heads per KV head, whose per-head registers would not fit the
-// 128 per lane a 1024-lane workgroup allows.
-__host__ __device__ constexpr int dec_waves(int G) { return G <= 4 ? 16 : 8; }
+constexpr int DEC_CHUNK = 64;                    // slots per workgroup
+// Waves per workgroup: 8, of 8 slot rows each.  64-slot chunks give 264
+// workgroups at one batch row, 8 KV heads and a 2048-token budget, enough to
+// reach every CU; 128-slot chunks left half of them idle (16.0 against
+// 14.3 us per step).
+__host__ __device__ constexpr int dec_waves(int) { return 8; }
 constexpr int DEC_MAX_SLOTS = (1 << 20) + 1;     // the C-ABI allows s + w + k <= 2^20
 constexpr int DEC_MAX_CHUNKS = (DEC_MAX_SLOTS + DEC_CHUNK - 1) / DEC_CHUNK;
 
@@ -338,12 +339,20 @@ __global__ void __launch_bounds__(dec_waves(G) * 64) decode_step_kernel(DecParam
   // 2. wave g: maximum and sum of exponentials of head g over the chunk
   if (wave < G) {
     const int g = wave;
-    const float x0 = lg[g][lane], x1 = lg[g][lane + 64];
-    float m = fmaxf(x0, x1);
+    constexpr int PER = DEC_CHUNK / 64;  // logits per lane
+    float xs[PER];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      xs[u] = lg[g][lane + 64 * u];
+      m = fmaxf(m, xs[u]);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     const float mu = m == -INFINITY ? 0.f : m;
-    float l = exp2f(x0 - mu) + exp2f(x1 - mu);  // -inf: 0
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) l += exp2f(xs[u] - mu);  // -inf: 0
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
     if (lane == 0) {
