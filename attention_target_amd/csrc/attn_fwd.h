@@ -299,18 +299,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
     if constexpr (SPARSE) {
       const auto kr = make_rsrc(kbase, p.S * ROWB);
       const auto vr = make_rsrc(vbase, p.S * ROWB);
+      if (tile < full_tiles) {
+        // every row of an unmasked tile lies inside the list: only clamp
+        // the entry to S (row S starts at the buffer's end and reads zeros)
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) {
-        const int t = entry(kraw[k], tile, g_r[k]);
-        const int row = t >= 0 ? t * ROWB : 0x7fff0000;
-        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
-        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
+        for (int k = 0; k < LOADS; ++k) {
+          const int row = (int)min((unsigned)kraw[k], (unsigned)p.S) * ROWB;
+          lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
+          lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k) {
+          const int t = entry(kraw[k], tile, g_r[k]);
+          const int row = t >= 0 ? t * ROWB : 0x7fff0000;
+          lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
+          lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
+        }
       }
-      if (tid < KT) {
+      if (tid < KT && tile >= full_tiles) {
         // positions and ranks are read only by masked tiles
         const int t = entry(next_raw, tile, tid);
         my_kpos = t >= 0 ? t : INT32_MAX;
-        my_krank = (tile >= full_tiles && my_kpos != INT32_MAX) ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
+        my_krank = my_kpos != INT32_MAX ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
       }
     }
   };
