@@ -3,7 +3,9 @@
 // KVpop paper, Section 3: every KV head keeps s sink tokens, a protected
 // window of the w most recent tokens, and the k best eligible tokens by
 // static priority, so the per-head cache never exceeds B = s + w + k tokens
-// (Section 4.3 measures the resulting flat memory at decode time).  Each
+// (the paper text's results section, Inference efficiency and Fig. 4, and
+// Section 4.3 of the Korean summary measure the resulting flat memory at
+// decode time).  Each
 // step (Section 3.2, "Running top-k sparse attention"): the new token enters
 // the window; token d-w leaves it and competes for the top-k; if the top-k is
 // full and the newcomer beats the worst retained token, that token is

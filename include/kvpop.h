@@ -176,7 +176,9 @@ size_t kvpop_workspace_size(int32_t which, const kvpop_shape *shape, int32_t sin
  * priorities is used: pi(t) = y(t) + (lambda / decay_step) * t, computed in
  * fp32 as c = lambda / decay_step, then y + c * t, each operation rounded
  * (exact for lambda = 0 or decay_step = 1; otherwise the pages' own
- * approximation up to the decay-step discretization).  Order: priority
+ * approximation: it ranks like Eq. 5 except between tokens whose static
+ * priorities lie within lambda (decay_step - 1) / decay_step, where the
+ * whole-step decay can swap them).  Order: priority
  * descending, ties (and -0.0 vs +0.0) to the lower index, NaN as -inf.
  *
  *  target [B,Hkv,S] fp32            y, e.g. kvpop_future_target's output (AGG_MAX, mean)
@@ -223,8 +225,9 @@ size_t kvpop_boundary_loss_workspace_size(int32_t batch, int32_t n_kv_heads, int
 
 /*
  * Fixed-budget decoding (Section 3: sinks, protected window and top-k;
- * Section 3.2, "Running top-k sparse attention"; Section 4.3 measures the
- * resulting bounded cache).  The state holds, per (batch row, KV head),
+ * Section 3.2, "Running top-k sparse attention"; the paper text's results
+ * section, Inference efficiency and Fig. 4, and Section 4.3 of the Korean
+ * summary measure the resulting bounded cache).  The state holds, per (batch row, KV head),
  * sinks + window + topk slots of K and V plus bookkeeping; it is
  * caller-owned device memory of kvpop_decode_state_size() bytes, set up by
  * kvpop_decode_init().  kvpop_decode_step() appends token `position` (which

@@ -51,3 +51,18 @@ def brute_attention(q, k, v, cu=None, scale=None, window=0):
                 colmass[b][g][t] = math.fsum(
                     math.exp(logit[(d, t)] - lse[b][g][d]) for d in range(t + window, en[t]) if d >= t)
     return lse, out, colmass
+
+
+def brute_future_count(S, cu=None, window=0):
+    """N_t of the mean in [P] Section 3.1, Eq. 2, by counting: for every key t,
+    the number of query positions d of t's document with d >= t + w, found by
+    walking over every position d of the sequence."""
+    st, en = _docs(S, cu)
+    out = []
+    for t in range(S):
+        n = 0
+        for d in range(S):
+            if st[d] == st[t] and d >= t + window:
+                n += 1
+        out.append(n)
+    return out

@@ -144,8 +144,8 @@ def masked_attention(q, k, v, rank, cutoff, sinks: int, window: int, scale=None,
     """Attention restricted to the budget mask: for every query row d,
     O_d = sum_{t in M_d} softmax_t(s_{d,t}) v_t and L_d = ln sum_{t in M_d} exp(s_{d,t}).
 
-    The mask is per KV head ("each KV head retains ...", [P] Section 3) and
-    shared by the G query heads of the group.  `rank` and `cutoff` are
+    The mask is per KV head (the budget is kept per KV head, [P] Section 3)
+    and shared by the G query heads of the group.  `rank` and `cutoff` are
     [B, Hkv, S].  Only the columns that some row of a block keeps are
     multiplied (every other column is masked for the whole block).  An empty
     row gives L = -inf and O = 0.  Returns (out [B,Hq,S,D], lse [B,Hq,S]); rows

@@ -51,8 +51,9 @@ def doc_bounds(S: int, cu=None):
 
 
 def default_scale(D: int, scale: Optional[float]) -> float:
-    """Softmax scale: 1/sqrt(D) when not given (the pages only name the
-    "pre-softmax attention logit", [P] Section 3.2; 1/sqrt(D) is Qwen3's)."""
+    """Softmax scale: 1/sqrt(D) when not given (the pages speak of the logit
+    before the softmax without its scale, [P] Section 3.2; 1/sqrt(D) is
+    Qwen3's)."""
     return 1.0 / math.sqrt(D) if (scale is None or scale <= 0) else float(scale)
 
 

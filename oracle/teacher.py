@@ -8,8 +8,8 @@ KVpop paper, Section 3.1:
   * Eq. 5: the teacher ranks E_d by effective scores, the target y(t) minus a
     per-head decay lambda times the number of decay steps of size Delta the
     token has aged: y(t) - lambda * floor((d - t) / Delta).  (The formula is
-    stripped from the pages; this is the plainest reading of "decay factor"
-    and "decay step size" with the stated recency bias.)
+    stripped from the pages; this is the plainest reading of a per-head decay
+    factor applied once per decay step, with the stated recency bias.)
   * The teacher keeps the top-k of E_d; the boundary token t_bnd(d) is the
     last retained token under the teacher ranking (Eq. 6 context), and the
     label of the newly eligible token d-w is whether the teacher keeps it.
@@ -24,14 +24,19 @@ Ordering: effective score descending, ties to the lower index (the same rule
 as the budget mask's static ranks).
 
 Section 3.2 turns the per-query top-k into a running threshold over static
-priorities "up to the decay-step discretization": with the decay written as
-lambda*(d-t)/Delta the query-dependent part lambda*d/Delta is shared by all
-eligible tokens, leaving the static priority
+priorities, which the pages say holds only approximately because the decay
+is applied in whole steps: with the decay written as lambda*(d-t)/Delta the
+query-dependent part lambda*d/Delta is shared by all eligible tokens, leaving
+the static priority
     pi(t) = y(t) + (lambda / Delta) * t.
 `teacher_static` computes that form in float32, operation by operation
-(c = lambda / Delta, then c * t, then y + that), which is what the GPU does;
-it equals the exact Eq. 5 ranking when lambda = 0 or Delta = 1
-(`teacher_bruteforce` checks that).
+(c = lambda / Delta, then c * t, then y + that).  Against the floor form of
+Eq. 5 the difference of a token's two scores at query d is a shared term
+plus lambda * frac((d-t)/Delta), in [0, lambda (Delta-1)/Delta]: the two
+rankings agree whenever static priorities differ by more than that (always
+when lambda = 0 or Delta = 1), and only such near-ties can swap otherwise.
+tests/test_oracle_teacher.py pins both statements against
+`teacher_bruteforce`.
 """
 from __future__ import annotations
 

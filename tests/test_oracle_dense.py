@@ -191,6 +191,44 @@ def test_duplicated_heads_sum_equals_none_plus_log_g():
     assert np.allclose(tm[fin], tn[:, ::G][fin], atol=1e-12)
 
 
+# ---------------------------------------------------------------- N_t of the mean (Eq. 2)
+@settings(max_examples=80, deadline=None)
+@given(S=st.integers(1, 40), docs=st.integers(1, 5), w=st.integers(0, 45), seed=st.integers(0, 10_000))
+def test_future_count_against_counting(S, docs, w, seed):
+    """N_t (the number of future queries the mean of Eq. 2 divides by)
+    against an explicit count over all positions, including windows longer
+    than a document."""
+    cu = rand_cu(S, min(docs, S), seed)
+    got = dense.future_count(S, cu, w)
+    assert got.tolist() == brute.brute_future_count(S, cu, w)
+
+
+@pytest.mark.parametrize("S,docs,w", [(40, 1, 0), (40, 1, 5), (64, 3, 4), (33, 2, 40), (50, 4, 13)])
+def test_zero_queries_mean_closed_form(S, docs, w):
+    """Q = 0 with the mean of Eq. 2: every probability of query d is
+    1/(pos(d)+1), so the mean future mass of key t is
+    (sum over d in [t+w, docend) of 1/(pos(d)+1)) / len([t+w, docend)),
+    written here from the positions alone.  AGG_MAX with eps = 0 gives its
+    log (the G heads are identical), -inf for an empty range."""
+    B, Hq, Hkv, D = 1, 4, 2, 8
+    _, k, v = rand_problem(B, Hq, Hkv, S, D, 9)
+    q = np.zeros((B, Hq, S, D))
+    cu = rand_cu(S, docs, 4)
+    r = dense.attention_pass(q, k, None, cu=cu, window=w, need_output=False)
+    got = dense.target_from_colmass(r["colmass"], Hkv, cu, w, AGG_MAX, True, 0.0)
+    starts = [0] if cu is None else list(cu[:-1])
+    ends = [S] if cu is None else list(cu[1:])
+    for t in range(S):
+        m = max(i for i in range(len(starts)) if starts[i] <= t)
+        ds, de = starts[m], ends[m]
+        fut = range(t + w, de)
+        if len(fut) == 0:
+            assert np.all(np.isneginf(got[0, :, t])), t
+            continue
+        mean = math.fsum(1.0 / (d - ds + 1) for d in fut) / len(fut)
+        assert np.allclose(got[0, :, t], math.log(mean), atol=1e-12), (t, mean)
+
+
 def test_max_aggregation_matches_per_head_max():
     B, Hq, Hkv, S, D = 1, 4, 2, 50, 8
     q, k, v = rand_problem(B, Hq, Hkv, S, D, 13)

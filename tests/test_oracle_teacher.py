@@ -135,3 +135,83 @@ def test_boundary_loss_closed_forms_and_gradient():
         assert abs(fd - grad[t]) < 1e-6
     # the gradient sums to zero (every term moves two scores in opposite directions)
     assert abs(grad.sum()) < 1e-12
+
+
+def _kept_exact(y, d, s, w, k, lam, delta):
+    """The teacher's kept set at query d under Eq. 5's floor form, by sorting
+    E_d on (effective score descending, index ascending) in float64."""
+    toks = list(range(s, d - w + 1))
+    eff = {t: float(y[t]) - lam * math.floor((d - t) / delta) for t in toks}
+    return sorted(toks, key=lambda t: (-eff[t], t))[:max(k, 0)]
+
+
+@pytest.mark.parametrize("delta,lam,seed", [(16, 0.5, 0), (16, 1.5, 1), (8, 0.75, 2), (5, 3.0, 3)])
+def test_static_equals_bruteforce_with_separated_priorities(delta, lam, seed):
+    """Delta > 1.  Eq. 5's effective score minus the static priority
+    pi(t) = y(t) + (lambda/Delta) t is -lambda d/Delta (shared by every token
+    at query d) plus lambda * frac((d-t)/Delta), which lies in
+    [0, lambda (Delta-1)/Delta].  So when every two static priorities differ
+    by more than that, both forms order E_d the same way and the running
+    threshold reproduces the floor form exactly.  Priorities here are
+    distinct integers times a gap above lambda, and y is derived from them."""
+    rng = np.random.default_rng(40 + seed)
+    S, s, w, k = 160, 3, 9, 17
+    gap = 1.25 * lam + 0.25
+    pi = rng.permutation(S).astype(np.float64) * gap
+    y = (pi - (lam / delta) * np.arange(S)).astype(np.float32)
+    lab, bnd = teacher.teacher_bruteforce(y, s, w, k, lam=lam, delta=delta)
+    lab2, bnd2, _, _ = teacher.teacher_static(y, s, w, k, lam=lam, delta=delta)
+    assert np.array_equal(lab, lab2) and np.array_equal(bnd, bnd2)
+
+
+@pytest.mark.parametrize("delta,k,label_differs", [(4, 2, True), (16, 7, True), (16, 13, False), (4, 12, False)])
+def test_static_departure_is_confined_to_one_decay_step(delta, k, label_differs):
+    """Equal targets, Delta > 1: the floor form ties every token of one
+    decay step (ties to the lower index), while the static priorities
+    lambda t / Delta put the newest first.  Both keep min(k, |E_d|) tokens,
+    and the kept sets differ only inside the decay step of the floor form's
+    boundary token; the boundary tokens themselves lie in that step.  Every
+    query where the labels differ is recorded and checked against this: the
+    newly eligible token d-w is the newest of its step, so the labels differ
+    exactly when the top-k ends inside d-w's own step."""
+    S, s, w, lam = 120, 2, 5, 0.5
+    y = np.zeros(S, dtype=np.float32)
+    lab, bnd = teacher.teacher_bruteforce(y, s, w, k, lam=lam, delta=delta)
+    lab2, bnd2, _, _ = teacher.teacher_static(y, s, w, k, lam=lam, delta=delta)
+    differ = []
+    for d in range(S):
+        if d - w < s:
+            assert lab[d] == lab2[d] == -1
+            continue
+        ex = _kept_exact(y, d, s, w, k, lam, delta)
+        st_kept = sorted(range(s, d - w + 1), key=lambda t: -t)[:k]   # newest first
+        assert len(ex) == len(st_kept) == min(k, d - w - s + 1)
+        step = lambda t: (d - t) // delta
+        bstep = step(ex[-1])
+        assert step(bnd2[d]) == bstep == step(bnd[d])
+        for t in set(ex) ^ set(st_kept):
+            assert step(t) == bstep, (d, t)
+        if lab[d] != lab2[d]:
+            differ.append(d)
+            assert step(d - w) == bstep
+    assert bool(differ) == label_differs, differ
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_static_departure_bound_on_random_targets(seed):
+    """For any targets: whenever the floor form keeps a token a that the
+    static form drops in favour of b, their static priorities are within
+    lambda (Delta-1)/Delta (plus float32 rounding) of each other, i.e. only
+    near-ties can swap."""
+    rng = np.random.default_rng(70 + seed)
+    S, s, w, k, lam, delta = 140, 2, 6, 13, 0.8, 16
+    y = rng.standard_normal(S).astype(np.float32)
+    pri = teacher.static_priorities(y, lam, delta).astype(np.float64)
+    bound = lam * (delta - 1) / delta + 1e-5
+    for d in range(s + w, S):
+        ex = set(_kept_exact(y, d, s, w, k, lam, delta))
+        toks = list(range(s, d - w + 1))
+        st_kept = set(sorted(toks, key=lambda t: (-pri[t], t))[:k])
+        for a in ex - st_kept:
+            for b in st_kept - ex:
+                assert abs(pri[a] - pri[b]) <= bound, (d, a, b, pri[a] - pri[b])
