@@ -158,15 +158,59 @@ def _dev(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _require(name: str, t: torch.Tensor, dtype=None, shape=None):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+def _require(name: str, t: torch.Tensor, dtype=None, shape=None, device=None, placed=True):
+    """Shape and dtype, then contiguity, then (unless `placed` is False)
+    placement: a GPU tensor, on `device` when given."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if placed:
+        _placed(device, (name, t))
+
+
+def _placed(device, *named):
+    """Every given tensor is a GPU tensor, on `device` (or on the first one's
+    device).  Called after the shape checks, so that a shape mismatch is
+    reported as such whatever the device."""
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _require_qkv(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None):
+    """q [B, Hq, S, D]; k (and v) [B, Hkv, S, D] with the same B, S, D and
+    dtype, Hq a multiple of Hkv, all on q's device.  The kernels take B, S and
+    D from q and read K and V with them, so any other K/V shape would be read
+    out of bounds."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, Hq, S, D]")
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a 4-D tensor [B, Hkv, S, D]")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"n_q_heads ({Hq}) must be a multiple of n_kv_heads ({Hkv})")
+    for name, t in (("k", k), ("v", v)):
+        if t is not None and tuple(t.shape) != (B, Hkv, S, D):
+            raise ValueError(f"{name} must have shape {(B, Hkv, S, D)} to match q {tuple(q.shape)}, "
+                             f"got {tuple(t.shape)}")
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
+    _require("q", q, placed=False)
+    _require("k", k, q.dtype, (B, Hkv, S, D), placed=False)
+    if v is not None:
+        _require("v", v, q.dtype, (B, Hkv, S, D), placed=False)
 
 
 def _stream_ptr(t: torch.Tensor, stream: Optional[torch.cuda.Stream]):
@@ -199,20 +243,20 @@ def attn_fwd_lse(q, k, v, cu_seqlens=None, scale: float = 0.0, need_output: bool
                  stream: Optional[torch.cuda.Stream] = None):
     """Causal attention forward with per-query LSE (kvpop_attn_fwd_lse)."""
     lib = load()
-    _require("q", q)
-    _require("k", k, q.dtype)
-    _require("v", v, q.dtype, k.shape)
+    _require_qkv(q, k, v)
     B, Hq, S, D = q.shape
+    if lse is not None:
+        _require("lse", lse, torch.float32, (B, Hq, S), placed=False)
+    if out is not None:
+        _require("out", out, q.dtype, q.shape, placed=False)
+    _placed(q.device, ("q", q), ("k", k), ("v", v), ("lse", lse), ("out", out))
     made = []
     if lse is None:
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
         made.append(lse)
-    _require("lse", lse, torch.float32, (B, Hq, S))
     if need_output and out is None:
         out = torch.empty_like(q)
         made.append(out)
-    if out is not None:
-        _require("out", out, q.dtype, q.shape)
     packed = _Packed(cu_seqlens, q.device)
     sh = make_shape(q, k, packed, scale)
     _check(lib.kvpop_attn_fwd_lse(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -227,17 +271,20 @@ def future_target(q, k, lse, window: int, agg: Union[str, int] = "sum", mean_ove
     """Future-attention target by the transposed pass (kvpop_future_target)."""
     lib = load()
     a = _AGG_NAMES[agg] if isinstance(agg, str) else int(agg)
-    _require("q", q)
-    _require("k", k, q.dtype)
+    _require_qkv(q, k)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    _require("lse", lse, torch.float32, (B, Hq, S))
+    _require("lse", lse, torch.float32, (B, Hq, S), placed=False)
     Hout = Hq if a == AGG_NONE else Hkv
+    if out is not None:
+        _require("out", out, torch.float32, (B, Hout, S), placed=False)
+    if workspace is not None:
+        _require("workspace", workspace, torch.uint8, placed=False)
+    _placed(q.device, ("q", q), ("k", k), ("lse", lse), ("out", out), ("workspace", workspace))
     made = []
     if out is None:
         out = torch.empty(B, Hout, S, dtype=torch.float32, device=q.device)
         made.append(out)
-    _require("out", out, torch.float32, (B, Hout, S))
     packed = _Packed(cu_seqlens, q.device)
     sh = make_shape(q, k, packed, scale)
     need = int(lib.kvpop_workspace_size(CALL_FUTURE_TARGET, ctypes.byref(sh), 0, window, 0))
@@ -260,12 +307,18 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
     Returns (o, lse, rank, cutoff); rank and cutoff are None unless asked for.
     """
     lib = load()
-    _require("q", q)
-    _require("k", k, q.dtype)
-    _require("v", v, q.dtype, k.shape)
+    _require_qkv(q, k, v)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    _require("scores", scores, torch.float32, (B, Hkv, S))
+    _require("scores", scores, torch.float32, (B, Hkv, S), placed=False)
+    if out is not None:
+        _require("out", out, q.dtype, q.shape, placed=False)
+    if lse is not None:
+        _require("lse", lse, torch.float32, (B, Hq, S), placed=False)
+    if workspace is not None:
+        _require("workspace", workspace, torch.uint8, placed=False)
+    _placed(q.device, ("q", q), ("k", k), ("v", v), ("scores", scores), ("out", out), ("lse", lse),
+            ("workspace", workspace))
     made = []
     if out is None:
         out = torch.empty_like(q)
@@ -273,8 +326,6 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
     if lse is None:
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
         made.append(lse)
-    _require("out", out, q.dtype, q.shape)
-    _require("lse", lse, torch.float32, (B, Hq, S))
     rank = cutoff = None
     if return_rank_cutoff:
         rank = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
@@ -308,7 +359,9 @@ def teacher_labels(target: torch.Tensor, sinks: int, window: int, topk: int,
         raise ValueError("target must be [B, Hkv, S]")
     B, H, S = target.shape
     if decay_lambda is not None:
-        _require("decay_lambda", decay_lambda, torch.float32, (H,))
+        _require("decay_lambda", decay_lambda, torch.float32, (H,), target.device)
+    if workspace is not None:
+        _require("workspace", workspace, torch.uint8, device=target.device)
     label = torch.empty(B, H, S, dtype=torch.int32, device=target.device)
     bnd = torch.empty_like(label)
     rank = brank = None
@@ -339,10 +392,12 @@ def boundary_loss(pred: torch.Tensor, label: torch.Tensor, boundary: torch.Tenso
     if pred.dim() != 3:
         raise ValueError("pred must be [B, Hkv, S]")
     B, H, S = pred.shape
-    _require("label", label, torch.int32, pred.shape)
-    _require("boundary", boundary, torch.int32, pred.shape)
+    _require("label", label, torch.int32, pred.shape, pred.device)
+    _require("boundary", boundary, torch.int32, pred.shape, pred.device)
     if weight is not None:
-        _require("weight", weight, torch.float32, pred.shape)
+        _require("weight", weight, torch.float32, pred.shape, pred.device)
+    if workspace is not None:
+        _require("workspace", workspace, torch.uint8, device=pred.device)
     loss = torch.empty_like(pred)
     grad = torch.empty_like(pred)
     need = int(lib.kvpop_boundary_loss_workspace_size(B, H, S))
@@ -388,10 +443,15 @@ class DecodeCache:
         """q [B,Hq,D], k, v [B,Hkv,D] (the cache dtype), score [B,Hkv] fp32."""
         lib = load()
         sh = self.shape
-        _require("q", q, self.dtype, (sh.batch, sh.n_q_heads, sh.head_dim))
-        _require("k", k, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
-        _require("v", v, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim))
-        _require("score", score, torch.float32, (sh.batch, sh.n_kv_heads))
+        dev = self.state.device
+        _require("q", q, self.dtype, (sh.batch, sh.n_q_heads, sh.head_dim), dev)
+        _require("k", k, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim), dev)
+        _require("v", v, self.dtype, (sh.batch, sh.n_kv_heads, sh.head_dim), dev)
+        _require("score", score, torch.float32, (sh.batch, sh.n_kv_heads), dev)
+        if out is not None:
+            _require("out", out, self.dtype, q.shape, dev)
+        if lse is not None:
+            _require("lse", lse, torch.float32, (sh.batch, sh.n_q_heads), dev)
         made = []
         if out is None:
             out = torch.empty_like(q)
