@@ -36,7 +36,8 @@ EXPORTS = ("kvpop_attn_fwd_lse", "kvpop_future_target", "kvpop_budget_mask_fwd",
            "kvpop_workspace_size", "kvpop_status_str", "kvpop_last_error",
            "kvpop_teacher_labels", "kvpop_teacher_workspace_size",
            "kvpop_boundary_loss", "kvpop_boundary_loss_workspace_size",
-           "kvpop_decode_state_size", "kvpop_decode_init", "kvpop_decode_step")
+           "kvpop_decode_state_size", "kvpop_decode_init", "kvpop_decode_step",
+           "kvpop_budget_lists_layout")
 
 _AGG_NAMES = {"sum": AGG_SUM, "max": AGG_MAX, "none": AGG_NONE}
 
@@ -53,6 +54,13 @@ class DecodeShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("sinks", ctypes.c_int32), ("window", ctypes.c_int32), ("topk", ctypes.c_int32)]
+
+
+class ListsLayout(ctypes.Structure):
+    _fields_ = [("lists_offset", ctypes.c_size_t), ("lens_offset", ctypes.c_size_t),
+                ("lens_full_offset", ctypes.c_size_t), ("status_offset", ctypes.c_size_t),
+                ("n_query_blocks", ctypes.c_int32), ("query_block", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("tile_keys", ctypes.c_int32)]
 
 
 class KvpopError(RuntimeError):
@@ -101,6 +109,8 @@ def load():
     lib.kvpop_decode_init.restype = I
     lib.kvpop_decode_step.argtypes = [DP, P, Z, I, P, P, P, P, P, P, P]
     lib.kvpop_decode_step.restype = I
+    lib.kvpop_budget_lists_layout.argtypes = [SP, I, I, I, ctypes.POINTER(ListsLayout)]
+    lib.kvpop_budget_lists_layout.restype = I
     _lib = lib
     return lib
 
@@ -236,6 +246,17 @@ def workspace_size(which: int, q: torch.Tensor, k: torch.Tensor, cu_seqlens=None
     packed = _Packed(cu_seqlens, "cpu" if not q.is_cuda else q.device)
     sh = make_shape(q, k, packed, scale)
     return int(lib.kvpop_workspace_size(which, ctypes.byref(sh), sinks, window, topk))
+
+
+def budget_lists_layout(q, k, sinks: int, window: int, topk: int, cu_seqlens=None, scale: float = 0.0) -> dict:
+    """Where kvpop_budget_mask_fwd leaves its per-query-block key lists in its
+    workspace (kvpop_budget_lists_layout): byte offsets and sizes."""
+    lib = load()
+    packed = _Packed(cu_seqlens, "cpu" if not q.is_cuda else q.device)
+    sh = make_shape(q, k, packed, scale)
+    lay = ListsLayout()
+    _check(lib.kvpop_budget_lists_layout(ctypes.byref(sh), int(sinks), int(window), int(topk), ctypes.byref(lay)))
+    return {f: getattr(lay, f) for f, _ in ListsLayout._fields_}
 
 
 def attn_fwd_lse(q, k, v, cu_seqlens=None, scale: float = 0.0, need_output: bool = True,
@@ -467,7 +488,7 @@ class DecodeCache:
         return out, lse
 
 
-__all__ = ["load", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+__all__ = ["load", "budget_lists_layout", "ListsLayout", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
            "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
            "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
            "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]

@@ -140,6 +140,26 @@ size_t kvpop_workspace_size(int32_t which, const kvpop_shape *shape, int32_t sin
   }
 }
 
+kvpop_status kvpop_budget_lists_layout(const kvpop_shape *shape, int32_t sinks, int32_t window, int32_t topk,
+                                       kvpop_lists_layout *layout) {
+  kvpop::ShapeInfo s{};
+  kvpop_status st = check_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (layout == nullptr) return fail(KVPOP_EINVAL, "layout is NULL");
+  if (sinks < 0 || window < 0 || topk < 0)
+    return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
+  const kvpop::BudgetListsInfo li = kvpop::budget_lists_info(s, sinks, window, topk);
+  layout->lists_offset = li.lists;
+  layout->lens_offset = li.lens;
+  layout->lens_full_offset = li.lens_full;
+  layout->status_offset = li.status;
+  layout->n_query_blocks = li.nqb;
+  layout->query_block = li.QB;
+  layout->capacity = li.cap;
+  layout->tile_keys = li.tile;
+  return ok();
+}
+
 kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const void *k, const void *v,
                                 void *o, float *lse, void *hip_stream) {
   kvpop::ShapeInfo s{};

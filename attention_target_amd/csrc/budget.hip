@@ -37,7 +37,7 @@ constexpr int CUT_ALL = 2147483647;
 constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
-  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, total;
+  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, lstatus, total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
 
@@ -76,12 +76,27 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   lo.lists = take(BH * lo.nqb * (size_t)lo.cap * 4);
   lo.lens = take(BH * lo.nqb * 4);
   lo.lens_full = take(BH * lo.nqb * 4);
+  lo.lstatus = take(BH * lo.nqb * 4);
   lo.total = off;
   return lo;
 }
 
 size_t budget_workspace_bytes(const ShapeInfo &s, int sinks, int window, int topk) {
   return budget_layout(s, sinks, window, topk).total;
+}
+
+BudgetListsInfo budget_lists_info(const ShapeInfo &s, int sinks, int window, int topk) {
+  const BudgetLayout lo = budget_layout(s, sinks, window, topk);
+  BudgetListsInfo li{};
+  li.lists = lo.lists;
+  li.lens = lo.lens;
+  li.lens_full = lo.lens_full;
+  li.status = lo.lstatus;
+  li.nqb = lo.nqb;
+  li.QB = lo.QB;
+  li.cap = lo.cap;
+  li.tile = KVPOP_FWD_KT;
+  return li;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
@@ -467,7 +482,7 @@ __global__ void __launch_bounds__(256) rank_order(const int *rank, int *order, i
 
 struct ListParams {
   const int *rank, *order, *cutoff;
-  int *lists, *lens, *lens_full;
+  int *lists, *lens, *lens_full, *status;
   int S, sinks, window, topk, QB, nqb, cap;
 };
 
@@ -595,6 +610,10 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   if (tid == 0) {
     p.lens[bh * p.nqb + qb] = min(off_p + n_c, p.cap);
     p.lens_full[bh * p.nqb + qb] = min(off_f + n_wc, p.cap);
+    // 0 when the list is whole: bit 0 = entries past the capacity were
+    // dropped, bit 1 = the sweep found a different number of shared keys
+    // than the count the segment was laid out for
+    p.status[bh * p.nqb + qb] = (off_p + n_c > p.cap ? 1 : 0) | (off_f != a_end + n_bfull ? 2 : 0);
   }
 }
 
@@ -646,6 +665,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   lp.lists = reinterpret_cast<int *>(w + lo.lists);
   lp.lens = reinterpret_cast<int *>(w + lo.lens);
   lp.lens_full = reinterpret_cast<int *>(w + lo.lens_full);
+  lp.status = reinterpret_cast<int *>(w + lo.lstatus);
   lp.topk = topk;
   lp.S = s.S;
   lp.sinks = sinks;

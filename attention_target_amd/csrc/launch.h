@@ -33,6 +33,13 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
                                 hipStream_t st);
 
 size_t budget_workspace_bytes(const ShapeInfo &s, int sinks, int window, int topk);
+// Where kvpop_budget_mask_fwd leaves its per-query-block key lists in the
+// workspace (byte offsets) and how they are shaped.
+struct BudgetListsInfo {
+  size_t lists, lens, lens_full, status;
+  int nqb, QB, cap, tile;
+};
+BudgetListsInfo budget_lists_info(const ShapeInfo &s, int sinks, int window, int topk);
 hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const void *v,
                          const float *scores, int sinks, int window, int topk, void *o, float *lse,
                          int *rank_out, int *cutoff_out, void *ws, hipStream_t st);

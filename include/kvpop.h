@@ -159,6 +159,30 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
                                    size_t ws_bytes, void *hip_stream);
 
 /*
+ * Where a kvpop_budget_mask_fwd call with this shape and these budget
+ * parameters leaves its per-query-block key lists in its workspace, for
+ * inspection once the call has completed (every call rebuilds them).  Query
+ * block m covers positions [m * query_block, min(S, (m + 1) * query_block)).
+ * For batch row b, KV head h and block m, with i = (b * Hkv + h) *
+ * n_query_blocks + m, the workspace holds, at the given byte offsets:
+ *   int32 lists[i * capacity + j], j < lens[i]: the positions of the keys the
+ *     block's queries may keep; the first lens_full[i] are kept by every
+ *     query of the block, and whole tiles of tile_keys of them are attended
+ *     without a per-element mask;
+ *   int32 lens[i], lens_full[i];
+ *   int32 status[i]: 0 when the list is whole; bit 0 set when entries past
+ *     the capacity were dropped; bit 1 set when the number of keys kept by
+ *     every query differs from the count the list was laid out for.
+ * Returns KVPOP_EINVAL for an invalid shape or negative budget parameters.
+ */
+typedef struct {
+  size_t lists_offset, lens_offset, lens_full_offset, status_offset;
+  int32_t n_query_blocks, query_block, capacity, tile_keys;
+} kvpop_lists_layout;
+kvpop_status kvpop_budget_lists_layout(const kvpop_shape *shape, int32_t sinks, int32_t window,
+                                       int32_t topk, kvpop_lists_layout *layout);
+
+/*
  * Bytes of workspace the call `which` (KVPOP_CALL_*) needs for this shape
  * and these budget parameters (sinks, window and topk matter only for
  * KVPOP_CALL_BUDGET_MASK_FWD; pass 0 otherwise).  Returns 0 for an invalid

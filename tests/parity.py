@@ -9,7 +9,9 @@ Tolerances:
   sparse output       per output row (one query, one head): max |delta| <= 2e-2 * RMS of the
                       oracle row; bf16 rounding is relative to each row's own magnitude
   dense output        per element |delta O| <= 2^-7 * sum_t a_{d,t} |v_t| + 1e-6: P and O
-                      rounded to bf16 (unit roundoff 2^-8 each); fp32 outputs: 2^-16
+                      rounded to bf16 (unit roundoff 2^-8 each); fp32 outputs: 2^-16;
+                      and the sparse output's per-row bound as well, each element
+                      allowed its own final rounding (half an ulp of the reference)
   ranks, cutoffs      bit-exact
 """
 import numpy as np
@@ -71,18 +73,22 @@ def assert_out_bounded(gpu, ref, abs_ref, u=2.0 ** -8, what="out"):
     return worst
 
 
-def assert_out_close(gpu, ref, rel=OUT_REL_TOL, what="out"):
+def assert_out_close(gpu, ref, rel=OUT_REL_TOL, what="out", out_round=0.0):
     """Per output row (the head_dim vector O_d of one query of one head):
     max_j |delta O_dj| <= rel * RMS_j(O_ref,dj).  Rows whose reference is
-    exactly zero (nothing attended) must be exactly zero.  Returns the largest
-    ratio max|delta| / RMS over rows."""
+    exactly zero (nothing attended) must be exactly zero.  With `out_round`
+    (the output format's unit roundoff), each element may in addition carry
+    its own rounding to that format, half an ulp of the reference value.
+    Returns the largest ratio (max|delta| less that allowance) / RMS over rows."""
     g, r = as_np(gpu), as_np(ref)
     assert g.shape == r.shape, (what, g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite"
     D = r.shape[-1]
     g2, r2 = g.reshape(-1, D), r.reshape(-1, D)
     rms = np.sqrt(np.mean(r2 * r2, axis=1))
-    err = np.abs(g2 - r2).max(axis=1)
+    with np.errstate(divide="ignore"):
+        half_ulp = out_round * np.exp2(np.floor(np.log2(np.abs(r2))))
+    err = np.maximum(np.abs(g2 - r2) - half_ulp, 0.0).max(axis=1)
     zero = rms == 0
     assert np.all(err[zero] == 0), f"{what}: rows that attend nothing are not zero"
     ratio = err[~zero] / rms[~zero]
@@ -91,3 +97,14 @@ def assert_out_close(gpu, ref, rel=OUT_REL_TOL, what="out"):
     assert worst <= rel, (f"{what}: row max |delta| / row RMS = {worst:.3g} > {rel} "
                           f"(row {i}: err {err[~zero][i]:.3g}, rms {rms[~zero][i]:.3g})")
     return worst
+
+
+def assert_dense_out(gpu, ref, abs_ref, u=2.0 ** -8, what="out"):
+    """The dense forward's output under both bounds: the element-wise
+    rounding bound, and the per-row bound of the sparse output with each
+    element allowed its own final rounding to the output format (an element
+    several times its row's RMS carries half an ulp of itself, which a bound
+    relative to the RMS cannot hold: that alone reaches 1.6e-2 of the RMS on
+    the packed 16k workload).  Returns the worst ratio of each."""
+    return (assert_out_bounded(gpu, ref, abs_ref, u=u, what=what),
+            assert_out_close(gpu, ref, what=what, out_round=u))

@@ -20,12 +20,59 @@ def say(*a):
     sys.stdout.flush()
 
 
+def ws_int32(ws_cpu, offset, n):
+    return ws_cpu[offset: offset + 4 * n].view(torch.int32).numpy()
+
+
+def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut):
+    """The key lists the sparse forward gathered, read back from its
+    workspace, against the oracle's mask rows, for every query block of every
+    (batch row, KV head):
+      * status 0: nothing dropped at the capacity, shared count as laid out;
+      * no key listed twice, and the listed set is the union of the block's
+        mask rows (every key some query keeps), plus, with a zero window
+        only, positions inside the block that no query keeps (the list
+        covers the block's own positions whole; the mask drops them);
+      * the shared segment (attended without a mask in whole tiles) is
+        exactly the keys every query of the block keeps, outside the
+        positions (d0-w, d1-w], which are masked per query instead."""
+    lay = kv.budget_lists_layout(q, k, s, w, topk)
+    B, Hkv, S = r_rank.shape
+    nqb, QB, cap = lay["n_query_blocks"], lay["query_block"], lay["capacity"]
+    wsc = ws.cpu()
+    lists = ws_int32(wsc, lay["lists_offset"], B * Hkv * nqb * cap).reshape(B * Hkv, nqb, cap)
+    lens = ws_int32(wsc, lay["lens_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
+    lens_full = ws_int32(wsc, lay["lens_full_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
+    status = ws_int32(wsc, lay["status_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
+    assert np.all(status == 0), f"list status set for {np.count_nonzero(status)} blocks"
+    assert np.all(lens <= cap) and np.all(lens_full <= lens)
+    for bh in range(B * Hkv):
+        b, h = divmod(bh, Hkv)
+        rk, ct = r_rank[b, h], r_cut[b, h]
+        for qb in range(nqb):
+            d0, d1 = qb * QB, min(S - 1, qb * QB + QB - 1)
+            rows = budget.mask_rows(rk[:d1 + 1], ct, s, w, np.arange(d0, d1 + 1))
+            lst = lists[bh, qb, :lens[bh, qb]]
+            assert np.unique(lst).size == lst.size, (bh, qb, "duplicate keys")
+            union = np.nonzero(rows.any(axis=0))[0]
+            extra = np.setdiff1d(lst, union)
+            assert np.setdiff1d(union, lst).size == 0, (bh, qb, "kept keys missing from the list")
+            assert extra.size == 0 or (w == 0 and np.all((extra > d0) & (extra <= d1))), (bh, qb, "listed set")
+            t = np.arange(d1 + 1)
+            shared = rows.all(axis=0) & ((t <= d0 - w) | (t > d1 - w))
+            full = lists[bh, qb, :lens_full[bh, qb]]
+            assert np.array_equal(np.sort(full), np.nonzero(shared)[0]), (bh, qb, "shared segment")
+
+
 def check_budget(kv, q, k, v, scores, s, w, topk, heads=None, rows=None):
-    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, scores, s, w, topk)
+    need = kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=s, window=w, topk=topk)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, scores, s, w, topk, workspace=ws)
     torch.cuda.synchronize()
     r_rank, r_cut = budget.budget_reference(scores.cpu().numpy(), s, w, topk)
     assert np.array_equal(rank.cpu().numpy(), r_rank), "ranks differ"
     assert np.array_equal(cut.cpu().numpy(), r_cut), "cutoffs differ"
+    check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut)
     ro, rl = budget.masked_attention(dense.to_f64(q), dense.to_f64(k), dense.to_f64(v), r_rank, r_cut, s, w,
                                      heads=heads, rows=rows)
     if heads is None:
@@ -92,13 +139,92 @@ def test_budget_batch_of_sequences(kvpop_lib, dt):
 
 
 def test_budget_full_causal_equals_dense(kvpop_lib):
-    """S <= s + w + k: the budget mask is the full causal mask."""
+    """S <= s + w + k: the budget mask is the full causal mask.  Both paths
+    against the oracle's dense attention at the per-row output tolerance, and
+    their LSEs within 1e-4 of each other."""
     t = synth.make_qkv(1, 500, 8, 2, 128, "bf16", 3, device=DEV, with_scores=True)
     o, lse, _, _ = kvpop_lib.budget_mask_fwd(t["q"], t["k"], t["v"], t["scores"], 4, 128, 400)
     od, ld = kvpop_lib.attn_fwd_lse(t["q"], t["k"], t["v"])
     torch.cuda.synchronize()
+    r = dense.attention_pass(dense.to_f64(t["q"]), dense.to_f64(t["k"]), dense.to_f64(t["v"]))
     assert torch.allclose(lse, ld, atol=1e-4)
-    assert torch.allclose(o.float(), od.float(), atol=2e-2)
+    assert_lse_close(lse, r["lse"], what="budget lse")
+    assert_out_close(o, r["out"], what="budget out")
+    assert_out_close(od, r["out"], what="dense out")
+
+
+# Q = 0: every logit is 0, so each query's LSE is ln |M_d| and its output the
+# mean of V over M_d.  The count pins how many keys the kernel attended for
+# every row; the fp32 mean pins which (one key swapped for another moves the
+# mean by |v_a - v_b| / |M_d|, ~1e-3 at |M_d| = 2048, against fp32 rounding
+# of ~1e-7).
+ZERO_Q = [
+    # S, Hq, Hkv, D, dtype, s, w, k, score kind
+    (700, 8, 2, 128, "bf16", 2, 64, 100, "ties"),
+    (2500, 4, 1, 128, "bf16", 4, 128, 300, "normal"),
+    (513, 4, 4, 64, "f32", 0, 1, 7, "normal"),
+    (1500, 4, 2, 64, "f32", 4, 32, 200, "ties"),
+    (900, 4, 1, 64, "f32", 3, 0, 150, "increasing"),
+]
+
+
+def _scores(t, kind, S, Hkv):
+    sc = t["scores"]
+    if kind == "ties":
+        sc = torch.round(sc * 2) / 2
+    elif kind == "increasing":
+        sc = torch.linspace(-3, 3, S, device=DEV).expand(1, Hkv, S)
+    return sc.contiguous()
+
+
+def check_zero_q(kv, t, sc, s, w, kk, mean_checks=None):
+    q = torch.zeros_like(t["q"])
+    k, v = t["k"], t["v"]
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, sc, s, w, kk)
+    torch.cuda.synchronize()
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk)
+    assert np.array_equal(cut.cpu().numpy(), r_cut)
+    count = np.exp(lse.cpu().double().numpy())
+    want = np.minimum(np.arange(S) + 1, s + w + kk)       # row size, pinned on the oracle
+    # fp32 logarithm: relative error ~1e-6, against 1/|M_d| >= 4.9e-4 for one key more or less
+    rel = np.abs(count / want - 1.0)
+    assert rel.max() <= 2e-5, f"keys per row: worst relative deviation {rel.max():.3g}"
+    if t["q"].dtype == torch.float32:
+        # (heads, rows) pairs to compare; default every head on every row
+        for heads, mrows in (mean_checks or [([(0, g) for g in range(Hq)], None)]):
+            ro, _ = budget.masked_attention(np.zeros((B, Hq, S, D)), dense.to_f64(k), dense.to_f64(v), r_rank,
+                                            r_cut, s, w, heads=heads, rows=mrows)
+            rr = np.arange(S) if mrows is None else np.asarray(sorted(set(int(x) for x in mrows)))
+            for (b, g) in heads:
+                err = np.abs(o[b, g, rr].cpu().double().numpy() - ro[b, g, rr]).max()
+                assert err <= 1e-5, f"mean of V over the mask: head {g} max |delta| {err:.3g}"
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,dt,s,w,kk,kind", ZERO_Q)
+def test_budget_zero_queries_membership(kvpop_lib, S, Hq, Hkv, D, dt, s, w, kk, kind):
+    say(f"budget Q=0 S={S} Hq={Hq} Hkv={Hkv} D={D} {dt} s={s} w={w} k={kk} {kind}")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, dt, 300 + S, device=DEV, with_scores=True)
+    check_zero_q(kvpop_lib, t, _scores(t, kind, S, Hkv), s, w, kk)
+
+
+def test_budget32k_zero_queries_membership(kvpop_lib):
+    """The budget workload's shape (S=32768, 32q/8kv, s=4, w=128, k=1916) with
+    Q = 0: every row of every query head attends exactly min(d+1, 2048) keys
+    (bf16, D=128); and in fp32 at D=64 the output is the mean of V over
+    exactly the oracle's mask: every row of two KV heads' first query heads,
+    and 512 rows (first and last 64, 384 random) of one query head of each
+    other KV head."""
+    t = synth.make_workload("budget32k", device=DEV)
+    say("budget32k Q=0 bf16 count")
+    check_zero_q(kvpop_lib, t, t["scores"], t["sinks"], t["window"], t["topk"])
+    say("budget32k Q=0 fp32 D=64 mean")
+    t32 = synth.make_qkv(1, 32768, 32, 8, 64, "f32", 77, device=DEV, with_scores=True)
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([np.arange(64), np.arange(32768 - 64, 32768), rng.integers(0, 32768, 384)])
+    check_zero_q(kvpop_lib, t32, t32["scores"], 4, 128, 1916,
+                 mean_checks=[([(0, 0), (0, 20)], None), ([(0, 4 * h + h % 4) for h in (1, 2, 3, 4, 6, 7)], rows)])
 
 
 def test_budget_empty_rows(kvpop_lib):
