@@ -37,7 +37,8 @@ EXPORTS = ("kvpop_attn_fwd_lse", "kvpop_future_target", "kvpop_budget_mask_fwd",
            "kvpop_teacher_labels", "kvpop_teacher_workspace_size",
            "kvpop_boundary_loss", "kvpop_boundary_loss_workspace_size",
            "kvpop_decode_state_size", "kvpop_decode_init", "kvpop_decode_step",
-           "kvpop_budget_lists_layout")
+           "kvpop_budget_lists_layout", "kvpop_future_target_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _AGG_NAMES = {"sum": AGG_SUM, "max": AGG_MAX, "none": AGG_NONE}
 
@@ -109,6 +110,8 @@ def load():
     lib.kvpop_decode_init.restype = I
     lib.kvpop_decode_step.argtypes = [DP, P, Z, I, P, P, P, P, P, P, P]
     lib.kvpop_decode_step.restype = I
+    lib.kvpop_future_target_noalloc.argtypes = [SP, P, P, P, I, I, I, F, P, P]
+    lib.kvpop_future_target_noalloc.restype = I
     lib.kvpop_budget_lists_layout.argtypes = [SP, I, I, I, ctypes.POINTER(ListsLayout)]
     lib.kvpop_budget_lists_layout.restype = I
     _lib = lib
@@ -319,6 +322,31 @@ def future_target(q, k, lse, window: int, agg: Union[str, int] = "sum", mean_ove
     return out
 
 
+def future_target_noalloc(q, k, lse, window: int, out: torch.Tensor, agg: Union[str, int] = "sum",
+                          mean_over_queries: bool = False, eps: float = 0.0, cu_seqlens=None, scale: float = 0.0,
+                          stream: Optional[torch.cuda.Stream] = None):
+    """kvpop_future_target_noalloc: the target without a workspace (the
+    library's fixed per-GPU scratch is used).  `out` is caller-allocated
+    ([B, Hkv, S] for SUM/MAX, [B, Hq, S] for NONE); with `cu_seqlens`, pass
+    an int32 tensor already on the device's host side (its device copy is
+    made here).  Calls overlapping on one GPU race."""
+    lib = load()
+    a = _AGG_NAMES[agg] if isinstance(agg, str) else int(agg)
+    _require_qkv(q, k)
+    B, Hq, S, D = q.shape
+    Hout = Hq if a == AGG_NONE else k.shape[1]
+    _require("lse", lse, torch.float32, (B, Hq, S), placed=False)
+    _require("out", out, torch.float32, (B, Hout, S), placed=False)
+    _placed(q.device, ("q", q), ("k", k), ("lse", lse), ("out", out))
+    packed = _Packed(cu_seqlens, q.device)
+    sh = make_shape(q, k, packed, scale)
+    _check(lib.kvpop_future_target_noalloc(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), lse.data_ptr(), int(window),
+                                           a, int(bool(mean_over_queries)), float(eps), out.data_ptr(),
+                                           _stream_ptr(q, stream)))
+    _retain(stream, packed.dev)
+    return out
+
+
 def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: float = 0.0,
                     return_rank_cutoff: bool = True, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -488,7 +516,7 @@ class DecodeCache:
         return out, lse
 
 
-__all__ = ["load", "budget_lists_layout", "ListsLayout", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+__all__ = ["load", "future_target_noalloc", "NOALLOC_SCRATCH_BYTES", "budget_lists_layout", "ListsLayout", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
            "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
            "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
            "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]

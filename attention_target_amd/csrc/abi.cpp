@@ -202,6 +202,38 @@ kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const 
                   "kvpop_future_target launch");
 }
 
+kvpop_status kvpop_future_target_noalloc(const kvpop_shape *shape, const void *q, const void *k, const float *lse,
+                                         int32_t window, int32_t agg, int32_t mean_over_queries, float eps,
+                                         float *target, void *hip_stream) {
+  static_assert(KVPOP_NOALLOC_SCRATCH_BYTES == kvpop::kNoAllocScratchBytes, "header and library agree");
+  kvpop::ShapeInfo s{};
+  kvpop_status st = check_shape(shape, s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !lse || !target) return fail(KVPOP_EINVAL, "q, k, lse and target must be non-NULL");
+  if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"lse", lse, 4}, {"target", target, 4},
+                             {"cu_seqlens", s.cu, 4}})) != KVPOP_OK)
+    return st;
+  if (window < 0) return fail(KVPOP_EINVAL, "window must be >= 0 (got %d)", window);
+  if (agg != KVPOP_AGG_SUM && agg != KVPOP_AGG_MAX && agg != KVPOP_AGG_NONE)
+    return fail(KVPOP_EINVAL, "agg must be KVPOP_AGG_SUM, _MAX or _NONE (got %d)", agg);
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(KVPOP_EINVAL, "eps must be finite and >= 0");
+  if (kvpop::tgt_grid_blocks(s, window) > kvpop::kMaxGridBlocks)
+    return fail(KVPOP_EUNSUPPORTED, "the target pass would need %lld workgroups", kvpop::tgt_grid_blocks(s, window));
+  const size_t need = kvpop::tgt_workspace_bytes_for(s, agg);
+  if (need > kvpop::kNoAllocScratchBytes)
+    return fail(KVPOP_EUNSUPPORTED,
+                "this shape needs %zu bytes of scratch; the no-allocation target holds %zu (use "
+                "kvpop_future_target with a workspace)",
+                need, kvpop::kNoAllocScratchBytes);
+  if ((st = check_device()) != KVPOP_OK) return st;
+  void *scratch = nullptr;
+  hipError_t e = kvpop::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return from_hip(e, "kvpop_future_target_noalloc scratch lookup");
+  return from_hip(kvpop::launch_future_target(s, q, k, lse, window, agg, mean_over_queries != 0, eps, target,
+                                              scratch, (hipStream_t)hip_stream),
+                  "kvpop_future_target_noalloc launch");
+}
+
 kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, const void *k, const void *v,
                                    const float *scores, int32_t sinks, int32_t window, int32_t topk, void *o,
                                    float *lse, int32_t *rank_out, int32_t *cutoff_out, void *workspace,

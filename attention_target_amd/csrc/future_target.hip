@@ -36,6 +36,7 @@
 //  * Blocks are ordered (batch, KV head, document, chunk descending, key tile)
 //    and dealt out so that each XCD (one L2) receives a contiguous range:
 //    concurrently running blocks of an XCD share the same query chunk.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -392,15 +393,48 @@ int tgt_chunk(int max_doc) {
   return 1024;
 }
 
-// Workspace: per-chunk partial sums [B, Hq or Hkv, n_chunks, S], then the
-// normaliser in logit units -L/scale [B, Hq, S].
-static size_t tgt_partial_floats(const ShapeInfo &s) {
+// Workspace: per-chunk partial sums [B, Hp, n_chunks, S] (Hp = Hkv for the
+// SUM aggregation, which adds a group's query heads inside the kernel, else
+// Hq), then the normaliser in logit units -L/scale [B, Hq, S].  Every
+// partial the finalize step reads is written by the same call, so the
+// workspace needs no clearing.
+static size_t tgt_partial_floats(const ShapeInfo &s, int Hp) {
   const int DT = tgt_chunk(s.max_doc);
   const size_t nch_max = (size_t)((s.max_doc + DT - 1) / DT);
-  return (size_t)s.B * s.Hq * nch_max * s.S;
+  return (size_t)s.B * Hp * nch_max * s.S;
 }
+static int tgt_partial_heads(const ShapeInfo &s, int agg) { return agg == 0 ? s.Hkv : s.Hq; }
 size_t tgt_workspace_bytes(const ShapeInfo &s) {
-  return (tgt_partial_floats(s) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+  return (tgt_partial_floats(s, s.Hq) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+}
+size_t tgt_workspace_bytes_for(const ShapeInfo &s, int agg) {
+  return (tgt_partial_floats(s, tgt_partial_heads(s, agg)) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+}
+
+// Scratch of the no-allocation entry point (kvpop_future_target_noalloc):
+// one array per GPU, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it only stands for the symbol):
+// each device's address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and kernels receive that address.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 template <typename T, int D, bool SUM>
@@ -434,7 +468,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.q = q;
   tp.k = k;
   tp.part = reinterpret_cast<float *>(ws);
-  float *nl = tp.part + tgt_partial_floats(s);
+  float *nl = tp.part + tgt_partial_floats(s, tgt_partial_heads(s, agg));
   tp.nl = nl;
   tp.B = s.B;
   tp.S = s.S;
@@ -466,7 +500,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.blocks_per_seq = (int)per_seq;
   tp.total_blocks = (int)(per_seq * s.B * s.Hkv);
   const bool sum = (agg == 0);
-  tp.Hp = sum ? s.Hkv : s.Hq;
+  tp.Hp = tgt_partial_heads(s, agg);
   hipError_t e = hipSuccess;
   if (tp.total_blocks > 0) {
     const size_t count = (size_t)s.B * s.Hq * s.S;

@@ -27,7 +27,13 @@ long long tgt_grid_blocks(const ShapeInfo &s, int window);
 hipError_t launch_fwd(const ShapeInfo &s, const void *q, const void *k, const void *v, void *o,
                       float *lse, hipStream_t st);
 
-size_t tgt_workspace_bytes(const ShapeInfo &s);
+size_t tgt_workspace_bytes(const ShapeInfo &s);             // enough for every aggregation
+size_t tgt_workspace_bytes_for(const ShapeInfo &s, int agg);  // what one aggregation uses
+// The no-allocation target's scratch: a fixed array per device, and its
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t noalloc_scratch(void **out);
 hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k, const float *lse,
                                 int window, int agg, int mean, float eps, float *target, void *ws,
                                 hipStream_t st);

@@ -126,6 +126,26 @@ kvpop_status kvpop_future_target(const kvpop_shape *shape, const void *q, const 
                                  void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * kvpop_future_target without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, layouts,
+ * results (bit for bit) and errors as kvpop_future_target, minus the
+ * workspace: the call uses a fixed scratch array of
+ * KVPOP_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends, and calls no allocator.  A shape whose scratch
+ * need (the partial sums [B, Hkv (SUM) or Hq, chunks, S] fp32 plus
+ * [B, Hq, S] fp32) exceeds it returns KVPOP_EUNSUPPORTED with the sizes in
+ * kvpop_last_error().  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.  Call with the stream's device current.
+ */
+#define KVPOP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kvpop_status kvpop_future_target_noalloc(const kvpop_shape *shape, const void *q, const void *k,
+                                         const float *lse, int32_t window, int32_t agg,
+                                         int32_t mean_over_queries, float eps, float *target,
+                                         void *hip_stream);
+
+/*
  * Fixed-budget sparse attention forward (Section 3 budget; Section 3.2
  * "Running top-k sparse attention").  Per KV head (shared by its query
  * heads), query d keeps

@@ -184,6 +184,28 @@ static void target_cases() {
   expect("window at INT32_MAX", tgt(&s, INT32_MAX), KVPOP_OK);
 }
 
+static void noalloc_cases() {
+  kvpop_shape s = shape();
+  auto call = [&](const kvpop_shape *sh, int window, int agg, float eps, const void *q, float *lse) {
+    return kvpop_future_target_noalloc(sh, q, P(), lse, window, agg, 0, eps, F(), nullptr);
+  };
+  expect("valid no-allocation target", call(&s, 4, KVPOP_AGG_SUM, 0.f, P(), F()), KVPOP_OK);
+  expect("no-allocation null q", call(&s, 4, KVPOP_AGG_SUM, 0.f, nullptr, F()), KVPOP_EINVAL);
+  expect("no-allocation null lse", call(&s, 4, KVPOP_AGG_SUM, 0.f, P(), nullptr), KVPOP_EINVAL);
+  expect("no-allocation misaligned q", call(&s, 4, KVPOP_AGG_SUM, 0.f, P(8), F()), KVPOP_EINVAL);
+  expect("no-allocation negative window", call(&s, -2, KVPOP_AGG_SUM, 0.f, P(), F()), KVPOP_EINVAL);
+  expect("no-allocation agg 5", call(&s, 4, 5, 0.f, P(), F()), KVPOP_EINVAL);
+  expect("no-allocation eps NaN", call(&s, 4, KVPOP_AGG_SUM, std::nanf(""), P(), F()), KVPOP_EINVAL);
+  expect("no-allocation null shape", call(nullptr, 4, KVPOP_AGG_SUM, 0.f, P(), F()), KVPOP_EINVAL);
+  // the stand-in sizes grow as B * heads * S * 64 bytes: 2^20 positions at 2 KV heads exceed 64 MiB
+  kvpop_shape big = shape(1, 1 << 20, 4, 2, 128);
+  expect("no-allocation beyond the scratch", call(&big, 4, KVPOP_AGG_SUM, 0.f, P(), F()), KVPOP_EUNSUPPORTED);
+  kvpop_shape mid = shape(1, (1 << 18) + (1 << 16), 4, 2, 128);
+  expect("no-allocation SUM within the scratch", call(&mid, 4, KVPOP_AGG_SUM, 0.f, P(), F()), KVPOP_OK);
+  expect("no-allocation per-head beyond the scratch", call(&mid, 4, KVPOP_AGG_NONE, 0.f, P(), F()),
+         KVPOP_EUNSUPPORTED);
+}
+
 static void budget_cases() {
   kvpop_shape s = shape();
   expect("valid budget", bud(&s), KVPOP_OK);
@@ -314,6 +336,7 @@ int main() {
   packed_cases();
   pointer_cases();
   target_cases();
+  noalloc_cases();
   budget_cases();
   size_cases();
   teacher_loss_cases();

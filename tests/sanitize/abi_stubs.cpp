@@ -32,6 +32,15 @@ hipError_t launch_fwd(const ShapeInfo &, const void *, const void *, const void 
   return hipSuccess;
 }
 size_t tgt_workspace_bytes(const ShapeInfo &) { return kStubWorkspace; }
+size_t tgt_workspace_bytes_for(const ShapeInfo &s, int agg) {
+  // grows with the shape so that the driver can ask for more than the scratch holds
+  return (size_t)s.B * (agg == 0 ? s.Hkv : s.Hq) * (size_t)s.S * 64;
+}
+hipError_t noalloc_scratch(void **out) {
+  static unsigned char fake[256];
+  *out = fake;
+  return hipSuccess;
+}
 hipError_t launch_future_target(const ShapeInfo &, const void *, const void *, const float *, int, int, int, float,
                                 float *, void *, hipStream_t) {
   ++g_stub_launches;
