@@ -22,6 +22,15 @@ tokens with rank <= c_d.
 Cutoff conventions (the pages leave them open): when |E_d| < k every eligible
 token is kept and c_d = CUTOFF_ALL (2^31 - 1); when k = 0 none is and
 c_d = CUTOFF_NONE (-1).
+
+Packed sequences (`cu`, document offsets; [P] Section 4 trains on packed
+sequences): attention never leaves a document, so the mask of a query is the
+mask its document would give on its own: sinks are the first s positions of
+the document and E_d = [start(d) + s, d - w] (the pages do not say; this is
+the reading under which packing changes nothing).  Ranks are taken over the
+whole packed sequence: restricted to one document they order its tokens
+exactly as the document's own ranks would, so c_d, the k-th smallest rank in
+E_d, selects the same tokens.
 """
 from __future__ import annotations
 
@@ -29,7 +38,7 @@ from typing import Optional
 
 import numpy as np
 
-from .dense import _row_lse, default_scale
+from .dense import _row_lse, default_scale, doc_bounds
 
 CUTOFF_ALL = 2 ** 31 - 1
 CUTOFF_NONE = -1
@@ -79,21 +88,27 @@ class _Fenwick:
         return pos          # 1-based position pos+1 -> rank pos
 
 
-def running_cutoffs(rank, sinks: int, window: int, topk: int) -> np.ndarray:
+def running_cutoffs(rank, sinks: int, window: int, topk: int, cu=None) -> np.ndarray:
     """c_d for every query position d, by the pages' sequential sweep.
 
-    At step d the token d - w becomes eligible when d - w >= s; its rank is
-    inserted into the Fenwick tree; then c_d is the k-th smallest inserted
-    rank (binary lifting) if at least k are inserted.
+    At step d the token d - w becomes eligible when d - w >= s (positions
+    counted from the start of d's document); its rank is inserted into the
+    Fenwick tree; then c_d is the k-th smallest inserted rank (binary
+    lifting) if at least k are inserted.  The tree starts empty at every
+    document start.
     """
     rank = [int(r) for r in rank]
     S = len(rank)
-    fw = _Fenwick(S)
+    start, _ = doc_bounds(S, cu)
+    fw = None
     count = 0
     out = np.empty(S, dtype=np.int64)
     for d in range(S):
+        if d == 0 or start[d] != start[d - 1]:
+            fw = _Fenwick(S)
+            count = 0
         t_new = d - window
-        if t_new >= sinks:
+        if t_new >= start[d] + sinks:
             fw.insert(rank[t_new])
             count += 1
         if topk <= 0:
@@ -105,32 +120,43 @@ def running_cutoffs(rank, sinks: int, window: int, topk: int) -> np.ndarray:
     return out
 
 
-def mask_rows(rank, cutoff, sinks: int, window: int, rows) -> np.ndarray:
+def mask_rows(rank, cutoff, sinks: int, window: int, rows, cu=None) -> np.ndarray:
     """Membership rows M_d over t (bool [len(rows), S]) from ranks and cutoffs:
-    t <= d and (t < s, or d - w < t, or (s <= t <= d - w and rank(t) <= c_d))."""
+    t in d's document, t <= d, and (t < a + s, or d - w < t, or
+    (a + s <= t <= d - w and rank(t) <= c_d)), where a is the start of d's
+    document (0 without `cu`).  `rank` may be cut short after the last row's
+    position; `cu` then still describes the whole sequence."""
     rank = np.asarray(rank)
     S = rank.shape[0]
     rows = np.asarray(rows)
     t = np.arange(S)[None, :]
     d = rows[:, None]
     c = np.asarray(cutoff)[rows][:, None]
-    sink = t < sinks
+    if cu is None:
+        a = np.zeros_like(d)
+    else:
+        c_ = [int(x) for x in cu]
+        a = np.asarray([max(x for x in c_[:-1] if x <= int(r)) for r in rows])[:, None]
+    sink = t < a + sinks
     win = t > d - window
-    elig = (t >= sinks) & (t <= d - window)
-    return (t <= d) & (sink | win | (elig & (rank[None, :] <= c)))
+    elig = (t >= a + sinks) & (t <= d - window)
+    return (t >= a) & (t <= d) & (sink | win | (elig & (rank[None, :] <= c)))
 
 
-def brute_mask_row(scores, d: int, sinks: int, window: int, topk: int) -> np.ndarray:
+def brute_mask_row(scores, d: int, sinks: int, window: int, topk: int, cu=None) -> np.ndarray:
     """The definition for one query, with no ranks and no running structure:
-    sinks, window, and the k best of E_d sorted by (score desc, index asc)."""
+    within d's document (starting at a), the sinks [a, a + s), the window
+    (d - w, d], and the k best of E_d = [a + s, d - w] sorted by
+    (score desc, index asc)."""
     s = np.asarray(scores, dtype=np.float64)
     S = s.shape[0]
+    a = 0 if cu is None else max(int(x) for x in list(cu)[:-1] if int(x) <= d)
     row = np.zeros(S, dtype=bool)
-    for t in range(min(sinks, d + 1)):
+    for t in range(a, min(a + sinks, d + 1)):
         row[t] = True
-    for t in range(max(0, d - window + 1), d + 1):
+    for t in range(max(a, d - window + 1), d + 1):
         row[t] = True
-    elig = list(range(sinks, d - window + 1))
+    elig = list(range(a + sinks, d - window + 1))
     key = [(-(s[t] if not np.isnan(s[t]) else -np.inf), t) for t in elig]
     key.sort()
     for _, t in key[:max(0, topk)]:
@@ -140,7 +166,7 @@ def brute_mask_row(scores, d: int, sinks: int, window: int, topk: int) -> np.nda
 
 def masked_attention(q, k, v, rank, cutoff, sinks: int, window: int, scale=None,
                      heads: Optional[list] = None, rows: Optional[np.ndarray] = None,
-                     row_block: int = 128):
+                     row_block: int = 128, cu=None):
     """Attention restricted to the budget mask: for every query row d,
     O_d = sum_{t in M_d} softmax_t(s_{d,t}) v_t and L_d = ln sum_{t in M_d} exp(s_{d,t}).
 
@@ -167,7 +193,7 @@ def masked_attention(q, k, v, rank, cutoff, sinks: int, window: int, scale=None,
         h = g // G
         for i0 in range(0, len(all_rows), row_block):
             rr = all_rows[i0:i0 + row_block]
-            M = mask_rows(rank[b, h], cutoff[b, h], sinks, window, rr)
+            M = mask_rows(rank[b, h], cutoff[b, h], sinks, window, rr, cu=cu)
             cols = np.nonzero(M.any(axis=0))[0]
             if cols.size == 0:
                 lse[b, g, rr] = -np.inf
@@ -183,8 +209,9 @@ def masked_attention(q, k, v, rank, cutoff, sinks: int, window: int, scale=None,
     return out, lse
 
 
-def budget_reference(scores, sinks: int, window: int, topk: int):
-    """ranks and cutoffs for scores [B, Hkv, S] (int64 arrays of the same shape)."""
+def budget_reference(scores, sinks: int, window: int, topk: int, cu=None):
+    """ranks and cutoffs for scores [B, Hkv, S] (int64 arrays of the same
+    shape); with `cu` (batch 1) the cutoffs restart at every document."""
     sc = np.asarray(scores, dtype=np.float64)
     B, H, S = sc.shape
     rank = np.empty((B, H, S), dtype=np.int64)
@@ -192,5 +219,5 @@ def budget_reference(scores, sinks: int, window: int, topk: int):
     for b in range(B):
         for h in range(H):
             rank[b, h] = static_ranks(sc[b, h])
-            cut[b, h] = running_cutoffs(rank[b, h], sinks, window, topk)
+            cut[b, h] = running_cutoffs(rank[b, h], sinks, window, topk, cu=cu)
     return rank, cut

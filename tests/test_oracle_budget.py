@@ -144,3 +144,54 @@ def test_empty_budget_rows():
 def test_nan_scores_rank_last():
     sc = np.array([np.nan, 1.0, -np.inf, 0.5, np.nan])
     assert budget.static_ranks(sc).tolist() == [2, 0, 3, 1, 4]
+
+
+# ---------------------------------------------------------------- packed sequences
+def _rand_cu(S, n_docs, r):
+    if n_docs <= 1 or S < 2:
+        return None
+    cuts = sorted(r.choice(np.arange(1, S), size=min(n_docs - 1, S - 1), replace=False).tolist())
+    return [0] + cuts + [S]
+
+
+@settings(max_examples=60, deadline=None)
+@given(S=st.integers(1, 120), docs=st.integers(1, 6), s=st.integers(0, 5), w=st.integers(0, 20),
+       k=st.integers(0, 30), ties=st.booleans(), seed=st.integers(0, 100000))
+def test_packed_sweep_equals_per_row_selection(S, docs, s, w, k, ties, seed):
+    """With documents, the sweep over global ranks that restarts at every
+    document gives, row by row, the per-row definition inside the row's
+    document (its own sinks, window and top-k)."""
+    r = np.random.default_rng(seed)
+    sc = r.integers(-3, 3, size=S).astype(np.float64) if ties else r.standard_normal(S)
+    cu = _rand_cu(S, docs, r)
+    rank = budget.static_ranks(sc)
+    cut = budget.running_cutoffs(rank, s, w, k, cu=cu)
+    rows = budget.mask_rows(rank, cut, s, w, np.arange(S), cu=cu)
+    for d in range(S):
+        assert np.array_equal(rows[d], budget.brute_mask_row(sc, d, s, w, k, cu=cu)), d
+
+
+@pytest.mark.parametrize("cu,s,w,k", [([0, 30, 47, 120], 3, 5, 9), ([0, 1, 2, 60, 61, 90], 2, 4, 6),
+                                      ([0, 64, 128], 0, 8, 20), ([0, 10, 90], 4, 0, 12)])
+def test_packed_equals_documents_alone(cu, s, w, k):
+    """Each document of a packed sequence gets exactly the mask, the output
+    and the LSE it gets when run alone (its own ranks, cutoffs and
+    positions from 0); rows of a packed sequence never reach another
+    document."""
+    S = cu[-1]
+    r = np.random.default_rng(sum(cu) + s + w + k)
+    sc = r.integers(-4, 4, size=(1, 1, S)).astype(np.float64)
+    Hq, D = 2, 8
+    q, kk, v = r.standard_normal((1, Hq, S, D)), r.standard_normal((1, 1, S, D)), r.standard_normal((1, 1, S, D))
+    rank, cut = budget.budget_reference(sc, s, w, k, cu=cu)
+    rows = budget.mask_rows(rank[0, 0], cut[0, 0], s, w, np.arange(S), cu=cu)
+    o, l = budget.masked_attention(q, kk, v, rank, cut, s, w, cu=cu, row_block=7)
+    for a, b in zip(cu[:-1], cu[1:]):
+        ra, ca = budget.budget_reference(sc[:, :, a:b], s, w, k)
+        alone = budget.mask_rows(ra[0, 0], ca[0, 0], s, w, np.arange(b - a))
+        assert not rows[a:b, :a].any() and not rows[a:b, b:].any()
+        assert np.array_equal(rows[a:b, a:b], alone)
+        oa, la = budget.masked_attention(q[:, :, a:b], kk[:, :, a:b], v[:, :, a:b], ra, ca, s, w)
+        assert np.allclose(o[:, :, a:b], oa, atol=1e-12) and np.allclose(l[:, :, a:b], la, atol=1e-12)
+        # row size: min(pos + 1, s + w + k) inside each document
+        assert np.array_equal(rows[a:b].sum(axis=1), np.minimum(np.arange(b - a) + 1, s + w + k))
