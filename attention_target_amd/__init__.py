@@ -350,7 +350,7 @@ def future_target_noalloc(q, k, lse, window: int, out: torch.Tensor, agg: Union[
 def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: float = 0.0,
                     return_rank_cutoff: bool = True, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    stream: Optional[torch.cuda.Stream] = None):
+                    stream: Optional[torch.cuda.Stream] = None, cu_seqlens=None):
     """Fixed-budget sparse attention forward (kvpop_budget_mask_fwd).
 
     Returns (o, lse, rank, cutoff); rank and cutoff are None unless asked for.
@@ -380,7 +380,7 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
         rank = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
         cutoff = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
         made += [rank, cutoff]
-    packed = _Packed(None, q.device)
+    packed = _Packed(cu_seqlens, q.device)
     sh = make_shape(q, k, packed, scale)
     need = int(lib.kvpop_workspace_size(CALL_BUDGET_MASK_FWD, ctypes.byref(sh), sinks, window, topk))
     if workspace is None:
@@ -390,7 +390,7 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
                                      scores.data_ptr(), int(sinks), int(window), int(topk), out.data_ptr(),
                                      lse.data_ptr(), _dev(rank), _dev(cutoff), workspace.data_ptr(),
                                      workspace.numel(), _stream_ptr(q, stream)))
-    _retain(stream, *made)
+    _retain(stream, packed.dev, *made)
     return out, lse, rank, cutoff
 
 

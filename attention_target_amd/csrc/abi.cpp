@@ -249,7 +249,6 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
     return st;
   if (sinks < 0 || window < 0 || topk < 0)
     return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
-  if (s.cu != nullptr) return fail(KVPOP_EUNSUPPORTED, "the budget mask does not support packed sequences");
   if (s.dtype == KVPOP_F32 && s.D != 64)
     return fail(KVPOP_EUNSUPPORTED, "the fp32 budget forward supports head_dim 64 only");
   if ((long long)s.S * s.D * (s.dtype == KVPOP_F32 ? 4 : 2) >= (1ll << 31))

@@ -139,7 +139,10 @@ __device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int j, i
   }
 }
 
-template <typename T, int D, bool WITH_O, bool SPARSE>
+// SPARSE_DOCS: the budget-masked forward over packed documents (the element
+// mask also checks the document and counts sinks from its start); a separate
+// instantiation, so that single-document calls keep the shorter mask.
+template <typename T, int D, bool WITH_O, bool SPARSE, bool SPARSE_DOCS = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_FWD_WAVES))) attn_fwd_kernel(const FwdParams p) {
   using Tiles = FwdTiles<T, D>;
   using KTile = SwizzledTile<T, D>;
@@ -203,6 +206,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
     n_tiles = (list_len + KT - 1) / KT;
     full_tiles = min(p.list_len_full[tile_id], list_len) / KT;
     cut_q = p.cutoff[bh_kv * p.S + qc];
+    if constexpr (SPARSE_DOCS) qdoc_start = find_doc(p.cu, p.n_docs, p.S, qc).start;
   }
 
   f32x16 o_acc[WITH_O ? NB : 1];
@@ -414,7 +418,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
                 } else {
                   const int t = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
                   const int rk = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
-                  ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+                  if constexpr (SPARSE_DOCS) {
+                    // same document, at or before the query, and a sink of
+                    // that document, in the window, or within the cutoff
+                    ok = qvalid && t <= qpos && t >= qdoc_start &&
+                         ((unsigned)(t - qdoc_start) < (unsigned)p.sinks || t > qpos - p.window || rk <= cut_q);
+                  } else {
+                    ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
+                  }
                 }
                 s[rb][i] = ok ? s[rb][i] : -INFINITY;
               }

@@ -207,12 +207,16 @@ __device__ __forceinline__ int block_excl_scan_1024(int x, int *sh_waves, int &t
   return before + incl - x;
 }
 
+// The wavelet matrix of one (batch, KV head) holds the ranks of positions
+// [base, S): base = sinks for an unpacked sequence (no eligible set starts
+// earlier), 0 for packed documents (each document's eligible set starts at
+// its own offset).
 struct WaveletParams {
   const int *rank;
   int *arr0, *arr1;
   uint32_t *bits;
   int *prefix, *zeros;
-  int S, sinks, L, nw1;
+  int S, base, L, nw1;
 };
 
 // One workgroup (1024 threads) per (batch, KV head): levels from the top bit
@@ -222,11 +226,11 @@ __global__ void __launch_bounds__(1024) budget_wavelet_build(const WaveletParams
   __shared__ int sh_waves[16];
   const size_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_e = p.S - p.sinks;
+  const int n_e = p.S - p.base;
   if (n_e <= 0) return;
   int *cur = p.arr0 + bh * p.S;
   int *nxt = p.arr1 + bh * p.S;
-  for (int i = tid; i < n_e; i += 1024) cur[i] = p.rank[bh * p.S + p.sinks + i];
+  for (int i = tid; i < n_e; i += 1024) cur[i] = p.rank[bh * p.S + p.base + i];
   __threadfence();
   __syncthreads();
   const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
@@ -311,10 +315,10 @@ __global__ void __launch_bounds__(1024) budget_wavelet_levels(const WaveletParam
   const int lvl = (int)blockIdx.x % p.L;
   const size_t bh = blockIdx.x / p.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_e = p.S - p.sinks;
+  const int n_e = p.S - p.base;
   if (n_e <= 0 || n_e > N_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
   {
-    const int *src = p.rank + bh * p.S + p.sinks;
+    const int *src = p.rank + bh * p.S + p.base;
     int r[WV_PER_THREAD];
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) r[j] = src[min(tid + 1024 * j, n_e - 1)];
@@ -422,7 +426,7 @@ __global__ void __launch_bounds__(1024) budget_wavelet_levels(const WaveletParam
 // The per-level LDS build when the eligible range fits (16 or 32 elements per
 // thread, whichever holds it), else the sequential global-memory build.
 static void launch_wavelet_build(const WaveletParams &wp, int BH, hipStream_t st) {
-  const int n_e = wp.S - wp.sinks;
+  const int n_e = wp.S - wp.base;
   const bool lds_ok = wp.S <= 65536 && wp.nw1 <= WV_LDS_WORDS;
   if (lds_ok && n_e <= 16 * 1024)
     hipLaunchKernelGGL(budget_wavelet_levels<16>, dim3(BH * wp.L), dim3(1024), 0, st, wp);
@@ -432,11 +436,11 @@ static void launch_wavelet_build(const WaveletParams &wp, int BH, hipStream_t st
     hipLaunchKernelGGL(budget_wavelet_build, dim3(BH), dim3(1024), 0, st, wp);
 }
 
-// k-th smallest (0-based kk) of the first m eligible ranks (positions
-// sinks .. sinks+m-1) on the wavelet matrix of (batch, KV head) bh.
-__device__ int wavelet_kth(const WaveletParams &p, size_t bh, int m, int kk) {
-  const int n_e = p.S - p.sinks;
-  int l = 0, r = m, val = 0;
+// k-th smallest (0-based kk) of the ranks of positions base+l .. base+r-1
+// on the wavelet matrix of (batch, KV head) bh.
+__device__ int wavelet_kth(const WaveletParams &p, size_t bh, int l, int r, int kk) {
+  const int n_e = p.S - p.base;
+  int val = 0;
   for (int lvl = p.L - 1; lvl >= 0; --lvl) {
     const uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
     const int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
@@ -459,15 +463,19 @@ __device__ int wavelet_kth(const WaveletParams &p, size_t bh, int m, int kk) {
   return val;
 }
 
-__global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, int window, int topk, int *cutoff) {
+// c_d: the topk-th smallest rank of E_d = [start(d) + sinks, d - window],
+// start(d) the first position of d's document.
+__global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, const int *cu, int n_docs, int sinks,
+                                                      int window, int topk, int *cutoff) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   const size_t bh = blockIdx.y;
   if (d >= p.S) return;
-  const long long m_e = (long long)d - window - p.sinks + 1;  // |E_d|
+  const int e_lo = find_doc(cu, n_docs, p.S, d).start + sinks;
+  const long long m_e = (long long)d - window - e_lo + 1;  // |E_d|
   int res;
   if (topk <= 0) res = CUT_NONE;
   else if (m_e < topk) res = CUT_ALL;
-  else res = wavelet_kth(p, bh, (int)m_e, topk - 1);
+  else res = wavelet_kth(p, bh, e_lo - p.base, e_lo - p.base + (int)m_e, topk - 1);
   cutoff[bh * p.S + d] = res;
 }
 
@@ -482,12 +490,17 @@ __global__ void __launch_bounds__(256) rank_order(const int *rank, int *order, i
 
 struct ListParams {
   const int *rank, *order, *cutoff;
+  const int *cu;  // document offsets, or nullptr for one document per batch row
   int *lists, *lens, *lens_full, *status;
-  int S, sinks, window, topk, QB, nqb, cap;
+  int S, n_docs, sinks, window, topk, QB, nqb, cap;
 };
 
-// Key list of query block [d0, d1], in two segments:
-//   full:    the sinks below the window, the eligible tokens of [s, d0-w]
+// Key list of query block [d0, d1].  Within a document starting at a, query d
+// keeps the sinks [a, a+s), its window (d-w, d] and the eligible tokens of
+// E_d = [a+s, d-w] with rank <= c_d.
+//
+// A block inside one document gets two segments:
+//   full:    the sinks below the window, the eligible tokens of [a+s, d0-w]
 //            with rank <= c_{d1}, then the positions (d1-w, d0].  Every query
 //            of the block keeps all of them (c_d is non-increasing, so
 //            c_{d1} <= c_d; and (d1-w, d0] is inside every query's window
@@ -499,9 +512,15 @@ struct ListParams {
 // The size of the full segment is known before the sweep: E_{d1} holds
 // exactly topk tokens of rank <= c_{d1}, so E_{d0} holds topk minus those in
 // (d0-w, d1-w] (at most QB-1 reads).
+// A block that spans documents lists, for each document's part [p0, p1],
+// the sinks below p0's window, the eligible tokens of E_{p0} with
+// rank <= c_{p0} and the positions (p0-w, p1] of the document, all in the
+// partial segment (the element mask also checks the document).  Only the
+// first part can reach back before d0, so the list still holds at most
+// s + k + w + QB - 1 keys.
 // The eligible tokens are found by whichever sweep is shorter: over the
-// positions [s, d0-w], or over the ranks [0, c_{d0}] through the inverse
-// permutation (late blocks: c_{d0} is about topk while d0-w grows with d0).
+// positions, or over the ranks [0, c] through the inverse permutation
+// (late blocks: c is about topk while the eligible range grows with d0).
 // The attention kernel needs no order inside a segment.
 __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   __shared__ int sh_w[2][4];
@@ -510,116 +529,156 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   const size_t bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d0 = qb * p.QB, d1 = min(p.S - 1, d0 + p.QB - 1);
-  const int c0 = p.cutoff[bh * p.S + d0];
-  const int c1 = p.cutoff[bh * p.S + d1];
   const int *rk = p.rank + bh * p.S;
   const int *ord = p.order + bh * p.S;
+  const int *cut = p.cutoff + bh * p.S;
   int *list = p.lists + (bh * p.nqb + qb) * (size_t)p.cap;
-  const int a_end = max(0, min(min(p.sinks, d0 - p.window + 1), d1 + 1));
-  const int b_hi = d0 - p.window;  // E_{d0} = [sinks, b_hi]
-  const int n_e0 = max(0, b_hi - p.sinks + 1);
-  int n_bfull;
-  if (c1 == CUT_NONE) {
-    n_bfull = 0;
-  } else if (c1 == CUT_ALL) {
-    n_bfull = n_e0;
-  } else {
-    if (tid == 0) sh_sub = 0;
-    __syncthreads();
-    const int lo = max(p.sinks, b_hi + 1), hi = d1 - p.window;  // E_{d1} \ E_{d0}
-    const int t = lo + tid;
-    if (t <= hi && rk[t] <= c1) atomicAdd(&sh_sub, 1);  // LDS counter, at most QB-1 increments
-    __syncthreads();
-    n_bfull = p.topk - sh_sub;
-  }
-  // the window region R = (d0-w, d1]: its part (d1-w, d0] lies inside every
-  // query's window and at or before every query of the block, so it joins
-  // the unmasked segment; the rest of R is masked per element
-  const int c_lo = max(0, d0 - p.window + 1);  // first position of R
-  const int wc_lo = max(c_lo, d1 - p.window + 1), wc_hi = d0;  // (d1-w, d0], possibly empty
-  const int n_wc = max(0, wc_hi - wc_lo + 1);
-  const int n_full = a_end + n_bfull + n_wc;
-  for (int i = tid; i < a_end && i < p.cap; i += 256) list[i] = i;
-  for (int i = tid; i < n_wc && a_end + n_bfull + i < p.cap; i += 256) list[a_end + n_bfull + i] = wc_lo + i;
-  int off_f = a_end, off_p = n_full;
-  // sweep length: positions [s, b_hi], or ranks [0, c0]
-  const bool by_rank = c0 != CUT_NONE && c0 != CUT_ALL && c0 + 1 < n_e0;
-  const int n_sweep = c0 == CUT_NONE ? 0 : (by_rank ? c0 + 1 : n_e0);
-  // the loads of up to LIST_PF chunks of 256 go out before the first chunk
-  // is used (one memory round trip per LIST_PF chunks, not per chunk)
-  constexpr int LIST_PF = 8;
-  for (int base0 = 0; base0 < n_sweep; base0 += 256 * LIST_PF) {
-    int tv[LIST_PF], rv[LIST_PF];
+  int off_f = 0, off_p = 0;
+
+  // Appends the eligible tokens t in [lo, hi] with rank <= c_any: those with
+  // rank <= c_all at off_f (full segment), the others at off_p (partial).
+  // The loads of up to LIST_PF chunks of 256 go out before the first chunk
+  // is used (one memory round trip per LIST_PF chunks, not per chunk).
+  auto sweep = [&](int lo, int hi, int c_all, int c_any) {
+    const int n_pos = max(0, hi - lo + 1);
+    if (n_pos == 0 || c_any == CUT_NONE) return;
+    const bool by_rank = c_any != CUT_ALL && c_any + 1 < n_pos;
+    const int n_sweep = by_rank ? c_any + 1 : n_pos;
+    constexpr int LIST_PF = 8;
+    for (int base0 = 0; base0 < n_sweep; base0 += 256 * LIST_PF) {
+      int tv[LIST_PF], rv[LIST_PF];
 #pragma unroll
-    for (int u = 0; u < LIST_PF; ++u) {
-      const int x = base0 + 256 * u + tid;
-      tv[u] = -1;
-      rv[u] = INT32_MAX;
-      if (x < n_sweep) {
-        if (by_rank) {
-          rv[u] = x;
-          tv[u] = ord[x];
-        } else {
-          tv[u] = p.sinks + x;
-          rv[u] = rk[tv[u]];
+      for (int u = 0; u < LIST_PF; ++u) {
+        const int x = base0 + 256 * u + tid;
+        tv[u] = -1;
+        rv[u] = INT32_MAX;
+        if (x < n_sweep) {
+          if (by_rank) {
+            rv[u] = x;
+            tv[u] = ord[x];
+          } else {
+            tv[u] = lo + x;
+            rv[u] = rk[tv[u]];
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < LIST_PF; ++u) {
-    if (base0 + 256 * u >= n_sweep) break;  // uniform over the workgroup
-    const int t = tv[u], r = rv[u];
-    const bool elig = t >= p.sinks && t <= b_hi;
-    const bool ff = elig && r <= c1;
-    const bool fp = elig && r > c1 && r <= c0;
-    const uint64_t mf = __ballot(ff), mp = __ballot(fp);
-    if (lane == 0) {
-      sh_w[0][wave] = __popcll(mf);
-      sh_w[1][wave] = __popcll(mp);
-    }
-    __syncthreads();
-    int bf = 0, bp = 0, tf = 0, tp = 0;
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) {
-        bf += sh_w[0][w];
-        bp += sh_w[1][w];
+      for (int u = 0; u < LIST_PF; ++u) {
+        if (base0 + 256 * u >= n_sweep) break;  // uniform over the workgroup
+        const int t = tv[u], r = rv[u];
+        const bool elig = t >= lo && t <= hi;
+        const bool ff = elig && r <= c_all;
+        const bool fp = elig && r > c_all && r <= c_any;
+        const uint64_t mf = __ballot(ff), mp = __ballot(fp);
+        if (lane == 0) {
+          sh_w[0][wave] = __popcll(mf);
+          sh_w[1][wave] = __popcll(mp);
+        }
+        __syncthreads();
+        int bf = 0, bp = 0, tf = 0, tp = 0;
+        for (int w = 0; w < 4; ++w) {
+          if (w < wave) {
+            bf += sh_w[0][w];
+            bp += sh_w[1][w];
+          }
+          tf += sh_w[0][w];
+          tp += sh_w[1][w];
+        }
+        if (ff) {
+          const int slot = off_f + bf + __popcll(mf & lanemask_lt(lane));
+          if (slot < p.cap) list[slot] = t;
+        }
+        if (fp) {
+          const int slot = off_p + bp + __popcll(mp & lanemask_lt(lane));
+          if (slot < p.cap) list[slot] = t;
+        }
+        off_f += tf;
+        off_p += tp;
+        __syncthreads();
       }
-      tf += sh_w[0][w];
-      tp += sh_w[1][w];
     }
-    if (ff) {
-      const int slot = off_f + bf + __popcll(mf & lanemask_lt(lane));
-      if (slot < p.cap) list[slot] = t;
+  };
+  // positions [lo, lo + n) at off_p, skipping [skip_lo, skip_lo + n_skip)
+  auto append_range = [&](int lo, int n, int skip_lo, int n_skip) {
+    for (int i = tid; i < n && off_p + i < p.cap; i += 256) {
+      const int t = (n_skip == 0 || lo + i < skip_lo) ? lo + i : lo + i + n_skip;
+      list[off_p + i] = t;
     }
-    if (fp) {
-      const int slot = off_p + bp + __popcll(mp & lanemask_lt(lane));
-      if (slot < p.cap) list[slot] = t;
+    off_p += n;
+  };
+
+  const Doc doc0 = find_doc(p.cu, p.n_docs, p.S, d0);
+  int status = 0;
+  if (d1 < doc0.end) {
+    // the block lies inside one document
+    const int a = doc0.start, e_lo = a + p.sinks;
+    const int c0 = cut[d0], c1 = cut[d1];
+    const int a_end = max(a, min(min(e_lo, d0 - p.window + 1), d1 + 1));  // sinks below the window: [a, a_end)
+    const int n_a = a_end - a;
+    const int b_hi = d0 - p.window;  // E_{d0} = [e_lo, b_hi]
+    const int n_e0 = max(0, b_hi - e_lo + 1);
+    int n_bfull;
+    if (c1 == CUT_NONE) {
+      n_bfull = 0;
+    } else if (c1 == CUT_ALL) {
+      n_bfull = n_e0;
+    } else {
+      if (tid == 0) sh_sub = 0;
+      __syncthreads();
+      const int lo = max(e_lo, b_hi + 1), hi = d1 - p.window;  // E_{d1} \ E_{d0}
+      const int t = lo + tid;
+      if (t <= hi && rk[t] <= c1) atomicAdd(&sh_sub, 1);  // LDS counter, at most QB-1 increments
+      __syncthreads();
+      n_bfull = p.topk - sh_sub;
     }
-    off_f += tf;
-    off_p += tp;
-    __syncthreads();
+    // the window region R = (d0-w, d1] of the document: its part (d1-w, d0]
+    // lies inside every query's window and at or before every query of the
+    // block, so it joins the unmasked segment; the rest of R is masked per
+    // element
+    const int c_lo = max(a, d0 - p.window + 1);                 // first position of R
+    const int wc_lo = max(c_lo, d1 - p.window + 1), wc_hi = d0;  // (d1-w, d0], possibly empty
+    const int n_wc = max(0, wc_hi - wc_lo + 1);
+    const int n_full = n_a + n_bfull + n_wc;
+    for (int i = tid; i < n_a && i < p.cap; i += 256) list[i] = a + i;
+    for (int i = tid; i < n_wc && n_a + n_bfull + i < p.cap; i += 256) list[n_a + n_bfull + i] = wc_lo + i;
+    off_f = n_a;
+    off_p = n_full;
+    sweep(e_lo, b_hi, c1, c0);
+    if (off_f != n_a + n_bfull) status |= 2;
+    // the masked part of R: all of R when (d1-w, d0] is empty, else
+    // (d0-w, d1-w] then (d0, d1]
+    append_range(c_lo, d1 - c_lo + 1 - n_wc, wc_lo, n_wc);
+    off_f += n_wc;
+  } else {
+    // the block spans documents: every part's keys are masked per element
+    for (int m_lo = doc0.start; m_lo <= d1;) {
+      const Doc dm = find_doc(p.cu, p.n_docs, p.S, m_lo);
+      const int a = dm.start, e_lo = a + p.sinks;
+      const int p0 = max(d0, a), p1 = min(d1, dm.end - 1);
+      const int a_end = max(a, min(min(e_lo, p0 - p.window + 1), p1 + 1));
+      append_range(a, a_end - a, 0, 0);
+      sweep(e_lo, p0 - p.window, CUT_NONE, cut[p0]);
+      const int c_lo = max(a, p0 - p.window + 1);
+      append_range(c_lo, max(0, p1 - c_lo + 1), 0, 0);
+      m_lo = dm.end;
     }
-  }
-  // the masked part of R: all of R when (d1-w, d0] is empty, else
-  // (d0-w, d1-w] then (d0, d1]
-  const int n_c = d1 - c_lo + 1 - n_wc;
-  for (int i = tid; i < n_c && off_p + i < p.cap; i += 256) {
-    const int t = (n_wc == 0 || c_lo + i < wc_lo) ? c_lo + i : c_lo + i + n_wc;
-    list[off_p + i] = t;
   }
   if (tid == 0) {
-    p.lens[bh * p.nqb + qb] = min(off_p + n_c, p.cap);
-    p.lens_full[bh * p.nqb + qb] = min(off_f + n_wc, p.cap);
+    p.lens[bh * p.nqb + qb] = min(off_p, p.cap);
+    p.lens_full[bh * p.nqb + qb] = min(off_f, p.cap);
     // 0 when the list is whole: bit 0 = entries past the capacity were
     // dropped, bit 1 = the sweep found a different number of shared keys
     // than the count the segment was laid out for
-    p.status[bh * p.nqb + qb] = (off_p + n_c > p.cap ? 1 : 0) | (off_f != a_end + n_bfull ? 2 : 0);
+    p.status[bh * p.nqb + qb] = status | (off_p > p.cap ? 1 : 0);
   }
 }
 
 template <typename T, int D>
 static hipError_t run_sparse(const FwdParams &fp, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, fp);
+  if (fp.cu != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true, true>), dim3(grid), dim3(256), 0, st, fp);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true, false>), dim3(grid), dim3(256), 0, st, fp);
   return hipGetLastError();
 }
 
@@ -648,11 +707,12 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   wp.prefix = reinterpret_cast<int *>(w + lo.prefix);
   wp.zeros = reinterpret_cast<int *>(w + lo.zeros);
   wp.S = s.S;
-  wp.sinks = sinks;
+  wp.base = s.cu != nullptr ? 0 : sinks;
   wp.L = lo.L;
   wp.nw1 = lo.nw1;
-  if (topk > 0 && s.S - sinks > 0) launch_wavelet_build(wp, BH, st);
-  hipLaunchKernelGGL(budget_cutoffs, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, wp, window, topk, cutoff);
+  if (topk > 0 && s.S - wp.base > 0) launch_wavelet_build(wp, BH, st);
+  hipLaunchKernelGGL(budget_cutoffs, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, wp, s.cu, s.n_docs, sinks, window,
+                     topk, cutoff);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -666,6 +726,8 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   lp.lens = reinterpret_cast<int *>(w + lo.lens);
   lp.lens_full = reinterpret_cast<int *>(w + lo.lens_full);
   lp.status = reinterpret_cast<int *>(w + lo.lstatus);
+  lp.cu = s.cu;
+  lp.n_docs = s.n_docs;
   lp.topk = topk;
   lp.S = s.S;
   lp.sinks = sinks;
@@ -690,8 +752,8 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   fp.G = s.Hq / s.Hkv;
   fp.HG = fwd_heads_per_block(fp.G);
   fp.scale_log2 = s.scale * kLog2e;
-  fp.cu = nullptr;
-  fp.n_docs = 1;
+  fp.cu = s.cu;
+  fp.n_docs = s.n_docs;
   fp.lists = lp.lists;
   fp.list_len = lp.lens;
   fp.list_len_full = lp.lens_full;
@@ -747,11 +809,11 @@ __global__ void __launch_bounds__(256) teacher_bounds(const TeacherParams p) {
   const size_t bh = blockIdx.y;
   const int S = p.wp.S;
   if (d >= S) return;
-  const long long m_e = (long long)d - p.window - p.wp.sinks + 1;  // |E_d|
+  const long long m_e = (long long)d - p.window - p.wp.base + 1;  // |E_d| (the matrix starts at the sinks)
   int lab = -1, bnd = -1, br = -1;
   if (p.topk > 0 && m_e > 0) {
     const int m = (int)m_e;
-    br = wavelet_kth(p.wp, bh, m, min(p.topk, m) - 1);
+    br = wavelet_kth(p.wp, bh, 0, m, min(p.topk, m) - 1);
     if (br >= 0 && br < S) bnd = p.order[bh * S + br];
     lab = (p.rank[bh * S + d - p.window] <= br) ? 1 : 0;
   }
@@ -819,7 +881,7 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   wp.prefix = reinterpret_cast<int *>(w + lo.prefix);
   wp.zeros = reinterpret_cast<int *>(w + lo.zeros);
   wp.S = S;
-  wp.sinks = sinks;
+  wp.base = sinks;
   wp.L = lo.L;
   wp.nw1 = lo.nw1;
   if (topk > 0 && S - sinks > 0) launch_wavelet_build(wp, BH, st);

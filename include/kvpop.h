@@ -158,11 +158,16 @@ kvpop_status kvpop_future_target_noalloc(const kvpop_shape *shape, const void *q
  *     rank(t) <= c_d.
  * It returns the attention output and natural-log LSE under that mask (the
  * sparse normaliser the paper reuses for its target).  A row with nothing
- * kept (sinks = window = topk = 0) gets lse = -inf and O = 0.
+ * kept (sinks = window = topk = 0) gets lse = -inf and O = 0.  Packed
+ * documents (cu_seqlens, Section 4 trains on packed sequences): every
+ * document keeps what it would keep on its own, with positions counted from
+ * its first token a: sinks [a, a + sinks), the window clipped at a, and
+ * E_d = [a + sinks, d - window].  rank_out then ranks the whole packed
+ * sequence (restricted to a document it orders that document's tokens as
+ * the document's own ranks would) and cutoff_out is in those ranks.
  *
- *  q, k, v                          inputs as for kvpop_attn_fwd_lse (cu_seqlens must be NULL;
- *                                   seqlen * head_dim * element size < 2^31 bytes, else
- *                                   KVPOP_EUNSUPPORTED)
+ *  q, k, v                          inputs as for kvpop_attn_fwd_lse (seqlen * head_dim *
+ *                                   element size < 2^31 bytes, else KVPOP_EUNSUPPORTED)
  *  scores [B,Hkv,S] fp32            static priorities
  *  sinks, window, topk >= 0
  *  o [B,Hq,S,D] (dtype), lse [B,Hq,S] fp32   outputs

@@ -110,6 +110,7 @@ static void packed_cases() {
     s.n_docs = 3;
     expect("valid packed forward", fwd(&s), KVPOP_OK);
     expect("valid packed target", tgt(&s), KVPOP_OK);
+    expect("valid packed budget", bud(&s), KVPOP_OK);
     s.batch = 2;
     expect("packed with batch 2", fwd(&s), KVPOP_EINVAL);
     s.batch = 1;

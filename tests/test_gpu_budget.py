@@ -24,7 +24,7 @@ def ws_int32(ws_cpu, offset, n):
     return ws_cpu[offset: offset + 4 * n].view(torch.int32).numpy()
 
 
-def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut):
+def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=None):
     """The key lists the sparse forward gathered, read back from its
     workspace, against the oracle's mask rows, for every query block of every
     (batch row, KV head):
@@ -36,7 +36,7 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut):
       * the shared segment (attended without a mask in whole tiles) is
         exactly the keys every query of the block keeps, outside the
         positions (d0-w, d1-w], which are masked per query instead."""
-    lay = kv.budget_lists_layout(q, k, s, w, topk)
+    lay = kv.budget_lists_layout(q, k, s, w, topk, cu_seqlens=cu)
     B, Hkv, S = r_rank.shape
     nqb, QB, cap = lay["n_query_blocks"], lay["query_block"], lay["capacity"]
     wsc = ws.cpu()
@@ -51,7 +51,7 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut):
         rk, ct = r_rank[b, h], r_cut[b, h]
         for qb in range(nqb):
             d0, d1 = qb * QB, min(S - 1, qb * QB + QB - 1)
-            rows = budget.mask_rows(rk[:d1 + 1], ct, s, w, np.arange(d0, d1 + 1))
+            rows = budget.mask_rows(rk[:d1 + 1], ct, s, w, np.arange(d0, d1 + 1), cu=cu)
             lst = lists[bh, qb, :lens[bh, qb]]
             assert np.unique(lst).size == lst.size, (bh, qb, "duplicate keys")
             union = np.nonzero(rows.any(axis=0))[0]
@@ -64,17 +64,19 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut):
             assert np.array_equal(np.sort(full), np.nonzero(shared)[0]), (bh, qb, "shared segment")
 
 
-def check_budget(kv, q, k, v, scores, s, w, topk, heads=None, rows=None):
-    need = kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=s, window=w, topk=topk)
+def check_budget(kv, q, k, v, scores, s, w, topk, heads=None, rows=None, cu=None):
+    """cu: None, or the document offsets as a list (batch 1)."""
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32)
+    need = kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, cu_seqlens=cu_t, sinks=s, window=w, topk=topk)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, scores, s, w, topk, workspace=ws)
+    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, scores, s, w, topk, workspace=ws, cu_seqlens=cu_t)
     torch.cuda.synchronize()
-    r_rank, r_cut = budget.budget_reference(scores.cpu().numpy(), s, w, topk)
+    r_rank, r_cut = budget.budget_reference(scores.cpu().numpy(), s, w, topk, cu=cu)
     assert np.array_equal(rank.cpu().numpy(), r_rank), "ranks differ"
     assert np.array_equal(cut.cpu().numpy(), r_cut), "cutoffs differ"
-    check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut)
+    check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=cu)
     ro, rl = budget.masked_attention(dense.to_f64(q), dense.to_f64(k), dense.to_f64(v), r_rank, r_cut, s, w,
-                                     heads=heads, rows=rows)
+                                     heads=heads, rows=rows, cu=cu)
     if heads is None:
         heads = [(b, g) for b in range(q.shape[0]) for g in range(q.shape[1])]
     rr = np.arange(q.shape[2]) if rows is None else np.asarray(sorted(set(int(x) for x in rows)))
@@ -177,17 +179,19 @@ def _scores(t, kind, S, Hkv):
     return sc.contiguous()
 
 
-def check_zero_q(kv, t, sc, s, w, kk, mean_checks=None):
+def check_zero_q(kv, t, sc, s, w, kk, mean_checks=None, cu=None):
     q = torch.zeros_like(t["q"])
     k, v = t["k"], t["v"]
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, sc, s, w, kk)
+    cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32)
+    o, lse, rank, cut = kv.budget_mask_fwd(q, k, v, sc, s, w, kk, cu_seqlens=cu_t)
     torch.cuda.synchronize()
-    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk)
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk, cu=cu)
     assert np.array_equal(cut.cpu().numpy(), r_cut)
     count = np.exp(lse.cpu().double().numpy())
-    want = np.minimum(np.arange(S) + 1, s + w + kk)       # row size, pinned on the oracle
+    start, _ = dense.doc_bounds(S, cu)
+    want = np.minimum(np.arange(S) - start + 1, s + w + kk)   # row size, pinned on the oracle
     # fp32 logarithm: relative error ~1e-6, against 1/|M_d| >= 4.9e-4 for one key more or less
     rel = np.abs(count / want - 1.0)
     assert rel.max() <= 2e-5, f"keys per row: worst relative deviation {rel.max():.3g}"
@@ -195,7 +199,7 @@ def check_zero_q(kv, t, sc, s, w, kk, mean_checks=None):
         # (heads, rows) pairs to compare; default every head on every row
         for heads, mrows in (mean_checks or [([(0, g) for g in range(Hq)], None)]):
             ro, _ = budget.masked_attention(np.zeros((B, Hq, S, D)), dense.to_f64(k), dense.to_f64(v), r_rank,
-                                            r_cut, s, w, heads=heads, rows=mrows)
+                                            r_cut, s, w, heads=heads, rows=mrows, cu=cu)
             rr = np.arange(S) if mrows is None else np.asarray(sorted(set(int(x) for x in mrows)))
             for (b, g) in heads:
                 err = np.abs(o[b, g, rr].cpu().double().numpy() - ro[b, g, rr]).max()
@@ -247,3 +251,54 @@ def test_budget32k(kvpop_lib):
     say("budget32k: gpu + oracle")
     check_budget(kvpop_lib, q, k, v, sc, t["sinks"], t["window"], t["topk"],
                  heads=[(0, g) for g in range(32)], rows=rows)
+
+
+# Packed documents: each document keeps what it would keep alone (sinks and
+# window counted from its start).  Document lengths include ones shorter
+# than a query block (32 positions), than the sinks plus window, and one.
+PACKED = [
+    # lengths, Hq, Hkv, D, dtype, s, w, k, score kind
+    ([700, 300, 1000], 8, 2, 128, "bf16", 4, 64, 100, "normal"),
+    ([5, 1, 40, 17, 250, 3, 90, 31, 63], 4, 1, 128, "bf16", 2, 16, 20, "ties"),
+    ([1200, 1300], 4, 2, 64, "f32", 3, 32, 150, "normal"),
+    ([333, 200, 480], 4, 1, 128, "bf16", 0, 0, 40, "normal"),
+    ([900, 100, 1000], 4, 1, 128, "bf16", 4, 128, 300, "increasing"),
+]
+
+
+def _cu(lengths):
+    return [0] + np.cumsum(lengths).tolist()
+
+
+@pytest.mark.parametrize("lengths,Hq,Hkv,D,dt,s,w,kk,kind", PACKED)
+def test_budget_packed(kvpop_lib, lengths, Hq, Hkv, D, dt, s, w, kk, kind):
+    S = sum(lengths)
+    say(f"budget packed docs={lengths} Hq={Hq} Hkv={Hkv} D={D} {dt} s={s} w={w} k={kk} {kind}")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, dt, 500 + S + kk, device=DEV, with_scores=True)
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], _scores(t, kind, S, Hkv), s, w, kk, cu=_cu(lengths))
+
+
+@pytest.mark.parametrize("lengths,dt", [([700, 300, 1000], "bf16"), ([5, 1, 40, 17, 250, 3, 90, 31, 63], "f32"),
+                                        ([1200, 1300], "f32")])
+def test_budget_packed_zero_queries_membership(kvpop_lib, lengths, dt):
+    S = sum(lengths)
+    say(f"budget packed Q=0 docs={lengths} {dt}")
+    D = 128 if dt == "bf16" else 64
+    t = synth.make_qkv(1, S, 8, 2, D, dt, 600 + S, device=DEV, with_scores=True)
+    check_zero_q(kvpop_lib, t, _scores(t, "ties", S, 2), 3, 24, 60, cu=_cu(lengths))
+
+
+def test_budget_packed16k(kvpop_lib):
+    """The pages' training shape: S=16384 packed as 6 documents, 32q/8kv/128,
+    with the budget s=4, w=128, k=1916: ranks, cutoffs and the key lists of
+    every block of every KV head exactly, output and LSE of every query head
+    on 512 sampled rows."""
+    t = synth.make_workload("packed16k", device=DEV)
+    cu = t["cu_seqlens"].tolist()
+    g = torch.Generator(device=DEV).manual_seed(16)
+    sc = torch.randn(1, 8, 16384, generator=g, device=DEV)
+    rng = np.random.default_rng(2)
+    rows = np.concatenate([np.arange(64), np.arange(16384 - 64, 16384), rng.integers(0, 16384, 384)])
+    say("budget packed16k docs", synth.doc_lengths_of(t["cu_seqlens"], 16384))
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], sc, 4, 128, 1916, heads=[(0, g_) for g_ in range(32)],
+                 rows=rows, cu=cu)
