@@ -139,8 +139,12 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
-class _Packed:
-    """Host and device copies of the document offsets (kept alive by the caller)."""
+class DocOffsets:
+    """Host and device copies of packed document offsets (cu_seqlens).
+
+    Every call that takes `cu_seqlens` accepts a list, a CPU tensor or a
+    DocOffsets; a DocOffsets made once and passed to repeated calls saves the
+    per-call device copy (the calls then allocate nothing for it)."""
 
     def __init__(self, cu_seqlens, device):
         if cu_seqlens is None:
@@ -152,8 +156,17 @@ class _Packed:
         self.dev = host.to(device)
         self.n_docs = int(host.numel()) - 1
 
+    def tolist(self):
+        return self.host.tolist()
 
-def make_shape(q: torch.Tensor, k: torch.Tensor, packed: _Packed, scale: float) -> Shape:
+
+def _Packed(cu_seqlens, device):
+    if isinstance(cu_seqlens, DocOffsets):
+        return cu_seqlens
+    return DocOffsets(cu_seqlens, device)
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, packed: DocOffsets, scale: float) -> Shape:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [B, H, S, D]")
     B, Hq, S, D = q.shape
@@ -350,10 +363,12 @@ def future_target_noalloc(q, k, lse, window: int, out: torch.Tensor, agg: Union[
 def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: float = 0.0,
                     return_rank_cutoff: bool = True, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    stream: Optional[torch.cuda.Stream] = None, cu_seqlens=None):
+                    stream: Optional[torch.cuda.Stream] = None, cu_seqlens=None, need_output: bool = True):
     """Fixed-budget sparse attention forward (kvpop_budget_mask_fwd).
 
     Returns (o, lse, rank, cutoff); rank and cutoff are None unless asked for.
+    With need_output=False only the mask is built (o and lse are None; the
+    key lists stay in `workspace`).
     """
     lib = load()
     _require_qkv(q, k, v)
@@ -369,12 +384,14 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
     _placed(q.device, ("q", q), ("k", k), ("v", v), ("scores", scores), ("out", out), ("lse", lse),
             ("workspace", workspace))
     made = []
-    if out is None:
+    if need_output and out is None:
         out = torch.empty_like(q)
         made.append(out)
-    if lse is None:
+    if need_output and lse is None:
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
         made.append(lse)
+    if not need_output:
+        out = lse = None
     rank = cutoff = None
     if return_rank_cutoff:
         rank = torch.empty(B, Hkv, S, dtype=torch.int32, device=q.device)
@@ -387,8 +404,8 @@ def budget_mask_fwd(q, k, v, scores, sinks: int, window: int, topk: int, scale: 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         made.append(workspace)
     _check(lib.kvpop_budget_mask_fwd(ctypes.byref(sh), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                     scores.data_ptr(), int(sinks), int(window), int(topk), out.data_ptr(),
-                                     lse.data_ptr(), _dev(rank), _dev(cutoff), workspace.data_ptr(),
+                                     scores.data_ptr(), int(sinks), int(window), int(topk), _dev(out),
+                                     _dev(lse), _dev(rank), _dev(cutoff), workspace.data_ptr(),
                                      workspace.numel(), _stream_ptr(q, stream)))
     _retain(stream, packed.dev, *made)
     return out, lse, rank, cutoff
@@ -516,7 +533,7 @@ class DecodeCache:
         return out, lse
 
 
-__all__ = ["load", "future_target_noalloc", "NOALLOC_SCRATCH_BYTES", "budget_lists_layout", "ListsLayout", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
+__all__ = ["load", "DocOffsets", "future_target_noalloc", "NOALLOC_SCRATCH_BYTES", "budget_lists_layout", "ListsLayout", "teacher_labels", "boundary_loss", "DecodeCache", "DecodeShape", "attn_fwd_lse", "future_target", "budget_mask_fwd", "workspace_size", "status_str",
            "last_error", "KvpopError", "Shape", "make_shape", "EXPORTS", "CUTOFF_ALL", "CUTOFF_NONE",
            "AGG_SUM", "AGG_MAX", "AGG_NONE", "CALL_FWD_LSE", "CALL_FUTURE_TARGET", "CALL_BUDGET_MASK_FWD",
            "OK", "EINVAL", "EUNSUPPORTED", "EWORKSPACE", "EHIP", "BF16", "F32"]

@@ -241,8 +241,9 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
   kvpop::ShapeInfo s{};
   kvpop_status st = check_shape(shape, s);
   if (st != KVPOP_OK) return st;
-  if (!q || !k || !v || !scores || !o || !lse)
-    return fail(KVPOP_EINVAL, "q, k, v, scores, o and lse must be non-NULL");
+  if (!q || !k || !v || !scores) return fail(KVPOP_EINVAL, "q, k, v and scores must be non-NULL");
+  if ((o == nullptr) != (lse == nullptr))
+    return fail(KVPOP_EINVAL, "o and lse must both be set, or both be NULL for the mask alone");
   if ((st = check_alignment({{"q", q, 16}, {"k", k, 16}, {"v", v, 16}, {"o", o, 16}, {"scores", scores, 4},
                              {"lse", lse, 4}, {"rank_out", rank_out, 4}, {"cutoff_out", cutoff_out, 4},
                              {"workspace", workspace, 16}})) != KVPOP_OK)

@@ -737,7 +737,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   lp.cap = lo.cap;
   hipLaunchKernelGGL(budget_lists, dim3(lo.nqb, BH), dim3(256), 0, st, lp);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || o == nullptr) return e;  // no outputs: the mask alone
 
   FwdParams fp{};
   fp.q = q;

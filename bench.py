@@ -62,15 +62,135 @@ def cpu_baseline(q, k, v, window, min_s: float = 10.0):
         dt += time.perf_counter() - t0
         assert np.isfinite(r["lse"]).all()
         heads += 1
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
     return {"value": heads * S / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
             "sample": f"layer 0, batch row 0, KV heads 0..{heads - 1} with their {G} query heads each: fp64 dense "
                       f"forward+LSE and target for {heads * S} keys at S={S} ({dt:.1f} s)",
-            "seconds": dt}
+            "seconds": dt, "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads)}
+
+
+def blas_threads() -> int:
+    """Threads of the BLAS the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def timed_calls(fns, reps: int, warm: int = 2):
+    """Median milliseconds of each callable in `fns`, run in turn `warm` +
+    `reps` times back to back on the current stream, HIP events between the
+    calls and one synchronisation at the end."""
+    stream = torch.cuda.current_stream()
+    n = len(fns)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(warm + reps)]
+    for i in range(warm + reps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    out = []
+    for j in range(n):
+        ms = sorted(e[j].elapsed_time(e[j + 1]) for e in ev[warm:])
+        out.append(ms[len(ms) // 2])
+    return out
+
+
+def config_line(kv, synth, dev, name: str, oracle_groups: int, reps: int = 10):
+    """One of the smaller workloads (a parity case, not the metric line):
+    the forward with LSE and the SUM target, each timed as back-to-back
+    calls; algorithmic flops from the actual document lengths; the fp64
+    oracle timed on `oracle_groups` KV-head groups of batch row 0."""
+    import numpy as np
+    from oracle import dense
+    t = synth.make_workload(name, device=dev)
+    q, k, v, w, cu = t["q"], t["k"], t["v"], t["window"], t["cu_seqlens"]
+    B_, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    lengths = synth.doc_lengths_of(cu, S)
+    o = torch.empty_like(q)
+    lse = torch.empty(B_, Hq, S, dtype=torch.float32, device=dev)
+    tgt = torch.empty(B_, Hkv, S, dtype=torch.float32, device=dev)
+    ws = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, q, k, cu_seqlens=cu, window=w), dtype=torch.uint8,
+                     device=dev)
+    cu_d = kv.DocOffsets(cu, dev) if cu is not None else None   # one device copy for all the timed calls
+    fwd = lambda: kv.attn_fwd_lse(q, k, v, cu_seqlens=cu_d, out=o, lse=lse)
+    tg = lambda: kv.future_target(q, k, lse, w, cu_seqlens=cu_d, out=tgt, workspace=ws)
+    fwd_ms, tgt_ms = timed_calls([fwd, tg], reps)
+    tflop = 2 * D * Hq * B_ * target_pairs(lengths, w)
+    fflop = 4 * D * Hq * B_ * causal_pairs(lengths)
+    elt = q.element_size()
+    fwd_bytes = (2 * q.numel() + 2 * k.numel()) * elt + lse.numel() * 4       # Q, K, V read; O, LSE written
+    tgt_bytes = (q.numel() + k.numel()) * elt + lse.numel() * 4 + tgt.numel() * 4
+    G = Hq // Hkv
+    groups = min(oracle_groups, Hkv)
+    t0 = time.perf_counter()
+    cl = None if cu is None else cu.tolist()
+    for h in range(groups):
+        r = dense.reference(q[0:1, h * G:(h + 1) * G].cpu(), k[0:1, h:h + 1].cpu(), v[0:1, h:h + 1].cpu(), cu=cl,
+                            window=w)
+        assert np.isfinite(r["lse"]).all()
+    osec = time.perf_counter() - t0
+    return {"workload": f"{name}: B={B_}, S={S}, {Hq}q/{Hkv}kv, D={D}, {str(q.dtype).replace('torch.', '')}, w={w}, "
+                        f"documents {lengths}",
+            "fwd_ms": round(fwd_ms, 4), "target_ms": round(tgt_ms, 4),
+            "fwd_tflops": round(fflop / (fwd_ms * 1e-3) / 1e12, 2),
+            "target_tflops": round(tflop / (tgt_ms * 1e-3) / 1e12, 2),
+            "fwd_frac_bf16_peak": round(fflop / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "target_frac_bf16_peak": round(tflop / (tgt_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "target_keys_per_s": round(B_ * Hkv * S / (tgt_ms * 1e-3), 1),
+            "fwd_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+            "target_gbs": round(tgt_bytes / (tgt_ms * 1e-3) / 1e9, 1),
+            "oracle": {"seconds": round(osec, 2), "keys_per_s": round(groups * S / osec, 1),
+                       "sample": f"batch row 0, {groups} of {Hkv} KV-head groups: fp64 forward, LSE and target",
+                       "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads()}}
+
+
+def budget_kernel_measurement(kv, synth, dev, reps: int = 10):
+    """The budget workload (S=32768, s=4, w=128, k=1916) split into the mask
+    construction alone (ranks, cutoffs, key lists: the call with no outputs)
+    and the whole call; the sparse attention kernel's time is their
+    difference.  The fp64 oracle (ranks, Fenwick cutoffs, masked attention of
+    one query head on 1024 rows) is timed alongside."""
+    import numpy as np
+    from oracle import budget, dense
+    t = synth.make_workload("budget32k", device=dev)
+    q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+    s_, w_, k_ = t["sinks"], t["window"], t["topk"]
+    B_, Hq, S, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B_, Hq, S, dtype=torch.float32, device=dev)
+    ws = torch.empty(kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=s_, window=w_, topk=k_),
+                     dtype=torch.uint8, device=dev)
+    full = lambda: kv.budget_mask_fwd(q, k, v, sc, s_, w_, k_, return_rank_cutoff=False, out=o, lse=lse,
+                                      workspace=ws)
+    mask = lambda: kv.budget_mask_fwd(q, k, v, sc, s_, w_, k_, return_rank_cutoff=False, workspace=ws,
+                                      need_output=False)
+    full_ms, mask_ms = timed_calls([full, mask], reps)
+    budget_ = s_ + w_ + k_
+    kept = sum(min(d + 1, budget_) for d in range(S))
+    flop = 4 * D * Hq * B_ * kept
+    attn_ms = full_ms - mask_ms
+    rows = np.arange(0, S, S // 1024)
+    t0 = time.perf_counter()
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s_, w_, k_)
+    G = Hq // k.shape[1]
+    budget.masked_attention(dense.to_f64(q[:, :G]), dense.to_f64(k[:, :1]), dense.to_f64(v[:, :1]), r_rank[:, :1],
+                            r_cut[:, :1], s_, w_, heads=[(0, 0)], rows=rows)
+    osec = time.perf_counter() - t0
+    return {"workload": f"budget32k: B={B_}, S={S}, {Hq}q/{k.shape[1]}kv, D={D}, bf16, sinks {s_}, window {w_}, "
+                        f"top-k {k_} (budget {budget_})",
+            "call_ms": round(full_ms, 4), "mask_ms": round(mask_ms, 4), "attention_ms": round(attn_ms, 4),
+            "attention_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+            "attention_frac_bf16_peak": round(flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "call_frac_bf16_peak": round(flop / (full_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "oracle": {"seconds": round(osec, 2),
+                       "sample": "ranks and Fenwick cutoffs of all 8 KV heads, masked attention of query head 0 on "
+                                 "1024 evenly spaced rows",
+                       "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads()},
+            "note": "attention_ms = whole call minus the mask-only call (both back to back); flops count kept pairs"}
 
 
 def budget_measurement(kv, synth, dev, reps: int = 10):
@@ -110,45 +230,64 @@ def budget_measurement(kv, synth, dev, reps: int = 10):
             "note": "whole call (ranks, cutoffs, lists, masked attention); flops count kept pairs only"}
 
 
-def paper_pipeline_measurement(kv, q, k, v, window: int, reps: int = 5):
+def paper_pipeline_measurement(kv, synth, dev, reps: int = 5):
     """Auxiliary (not part of `value`): the pages' training configuration of
-    the target on one layer of the metric workload: the budget-masked forward
-    (sinks 4, window w, top-k so that the budget is 2048, seeded N(0,1) static
-    scores) returns the sparse LSE, which feeds the transposed target pass
-    (Eq. 9 instead of the dense Eq. 8)."""
+    the target at its own shape, S=16384 packed as 6 documents (32q/8kv,
+    D=128, w=128), budget 4 + 128 + 1916 = 2048 with seeded N(0,1) static
+    scores: the budget-masked forward returns the sparse LSE L~, which feeds
+    the transposed target pass (Eq. 9 instead of the dense Eq. 8).  Reports
+    its time and how far its target lies from the dense-L target: |delta|
+    over keys whose dense mass exceeds e^-30, and the agreement of the teacher
+    labels (paper mode: max over the group of ln(mean + 1e-6), no decay) each
+    target gives, document by document."""
+    t = synth.make_workload("packed16k", device=dev)
+    q, k, v, w, cu = t["q"], t["k"], t["v"], t["window"], t["cu_seqlens"]
     B_, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    sinks, topk = 4, 2048 - 4 - window
-    g = torch.Generator(device=q.device).manual_seed(2048)
-    scores = torch.randn(B_, Hkv, S, generator=g, device=q.device, dtype=torch.float32)
+    sinks, topk = 4, 2048 - 4 - w
+    g = torch.Generator(device=dev).manual_seed(2048)
+    scores = torch.randn(B_, Hkv, S, generator=g, device=dev, dtype=torch.float32)
     o = torch.empty_like(q)
-    lse = torch.empty(B_, Hq, S, dtype=torch.float32, device=q.device)
-    tgt = torch.empty(B_, Hkv, S, dtype=torch.float32, device=q.device)
-    wsb = torch.empty(kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, sinks=sinks, window=window, topk=topk),
-                      dtype=torch.uint8, device=q.device)
-    wst = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, q, k, window=window), dtype=torch.uint8,
-                      device=q.device)
-    stream = torch.cuda.current_stream(q.device)
-    # iterations back to back (events between the calls, one synchronisation
-    # at the end), the first two untimed
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
-    for i in range(reps + 2):
-        ev[i][0].record(stream)
-        kv.budget_mask_fwd(q, k, v, scores, sinks, window, topk, return_rank_cutoff=False, out=o, lse=lse,
-                           workspace=wsb, stream=stream)
-        ev[i][1].record(stream)
-        kv.future_target(q, k, lse, window, out=tgt, workspace=wst, stream=stream)
-        ev[i][2].record(stream)
+    lse_sp = torch.empty(B_, Hq, S, dtype=torch.float32, device=dev)
+    lse_dn = torch.empty_like(lse_sp)
+    t_sp = torch.empty(B_, Hkv, S, dtype=torch.float32, device=dev)
+    t_dn = torch.empty_like(t_sp)
+    wsb = torch.empty(kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, cu_seqlens=cu, sinks=sinks, window=w,
+                                        topk=topk), dtype=torch.uint8, device=dev)
+    wst = torch.empty(kv.workspace_size(kv.CALL_FUTURE_TARGET, q, k, cu_seqlens=cu, window=w), dtype=torch.uint8,
+                      device=dev)
+    cu_d = kv.DocOffsets(cu, dev)
+    bud = lambda: kv.budget_mask_fwd(q, k, v, scores, sinks, w, topk, return_rank_cutoff=False, out=o, lse=lse_sp,
+                                     workspace=wsb, cu_seqlens=cu_d)
+    tsp = lambda: kv.future_target(q, k, lse_sp, w, out=t_sp, workspace=wst, cu_seqlens=cu_d)
+    fwd = lambda: kv.attn_fwd_lse(q, k, v, out=o, lse=lse_dn, cu_seqlens=cu_d)
+    tdn = lambda: kv.future_target(q, k, lse_dn, w, out=t_dn, workspace=wst, cu_seqlens=cu_d)
+    b_ms, ts_ms, f_ms, td_ms = timed_calls([bud, tsp, fwd, tdn], reps)
+    big = t_dn > -30.0
+    both = big & torch.isfinite(t_sp)
+    dev_abs = (t_sp - t_dn).abs()[both]
+    # teacher labels from each target in the paper's mode, per document
+    y_sp = kv.future_target(q, k, lse_sp, w, agg="max", mean_over_queries=True, eps=1e-6, cu_seqlens=cu)
+    y_dn = kv.future_target(q, k, lse_dn, w, agg="max", mean_over_queries=True, eps=1e-6, cu_seqlens=cu)
+    agree = total = 0
+    c = cu.tolist()
+    for a_, b_ in zip(c[:-1], c[1:]):
+        l_sp, _ = kv.teacher_labels(y_sp[:, :, a_:b_].contiguous(), sinks, w, topk)
+        l_dn, _ = kv.teacher_labels(y_dn[:, :, a_:b_].contiguous(), sinks, w, topk)
+        has = (l_dn >= 0) & (l_sp >= 0)
+        agree += int((has & (l_sp == l_dn)).sum())
+        total += int(has.sum())
     torch.cuda.synchronize()
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev[2:]]
-    tgt_ms = [e[1].elapsed_time(e[2]) for e in ev[2:]]
-    fwd_ms.sort()
-    tgt_ms.sort()
-    f, t_ = fwd_ms[len(fwd_ms) // 2], tgt_ms[len(tgt_ms) // 2]
-    return {"workload": f"one layer of the metric workload (B={B_}, S={S}, {Hq}q/{Hkv}kv, D={D}), budget "
-                        f"{sinks}+{window}+{topk}=2048, seeded N(0,1) scores; sparse LSE -> target",
-            "budget_fwd_ms": round(f, 4), "target_ms": round(t_, 4), "layer_ms": round(f + t_, 4),
-            "keys_per_s": round(B_ * Hkv * S / ((f + t_) * 1e-3), 1)}
+    return {"workload": f"packed16k: S={S} as documents {synth.doc_lengths_of(cu, S)}, {Hq}q/{Hkv}kv, D={D}, "
+                        f"w={w}, budget {sinks}+{w}+{topk}=2048, seeded N(0,1) scores",
+            "budget_fwd_ms": round(b_ms, 4), "target_sparse_lse_ms": round(ts_ms, 4),
+            "layer_ms": round(b_ms + ts_ms, 4), "keys_per_s": round(B_ * Hkv * S / ((b_ms + ts_ms) * 1e-3), 1),
+            "dense_fwd_ms": round(f_ms, 4), "target_dense_lse_ms": round(td_ms, 4),
+            "deviation_from_dense_target": {
+                "keys": int(both.sum()), "max_abs": round(float(dev_abs.max()), 5),
+                "mean_abs": round(float(dev_abs.mean()), 6),
+                "not_finite_with_sparse_lse": int((big & ~torch.isfinite(t_sp)).sum())},
+            "teacher_label_agreement": round(agree / max(total, 1), 6), "teacher_labels_compared": total}
 
 
 def teacher_measurement(kv, tgt, window: int, reps: int = 10):
@@ -381,12 +520,19 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
     if args.layers is None:
-        out["paper_pipeline"] = paper_pipeline_measurement(kv, layers[0]["q"], layers[0]["k"], layers[0]["v"], w)
         out["teacher_and_loss"] = teacher_measurement(kv, layers[0]["tgt"], w)
         layers.clear()
         torch.cuda.empty_cache()
         out["budget_path"] = budget_measurement(kv, synth, dev)
         out["decode"] = decode_measurement(kv, dev)
+        out["paper_pipeline"] = paper_pipeline_measurement(kv, synth, dev)
+        out["configs"] = {
+            "tiny": config_line(kv, synth, dev, "tiny", 1, reps=50),
+            "qwen4k": config_line(kv, synth, dev, "qwen4k", 2),
+            "packed16k": config_line(kv, synth, dev, "packed16k", 1),
+            "stack36": {"note": "the metric line itself (value, roofline, kernels, cpu_baseline)"},
+            "budget32k": budget_kernel_measurement(kv, synth, dev),
+        }
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

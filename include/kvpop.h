@@ -112,10 +112,15 @@ kvpop_status kvpop_attn_fwd_lse(const kvpop_shape *shape, const void *q, const v
  *                                   dense one from kvpop_attn_fwd_lse makes
  *                                   the identity exact; the sparse one from
  *                                   kvpop_budget_mask_fwd is the paper's
- *                                   approximation.  Precondition:
- *                                   s_{d,t} - lse_d < 88 (always true for the
- *                                   dense normaliser, which bounds every
- *                                   logit of its row).
+ *                                   approximation.  The masses are summed
+ *                                   in fp32 without a running maximum, so a
+ *                                   key whose summed mass exceeds FLT_MAX
+ *                                   (ln = 88.72, before any mean; possible
+ *                                   only when s_{d,t} - lse_d exceeds ~88 for
+ *                                   some d, never with the dense normaliser,
+ *                                   which bounds every logit of its row)
+ *                                   saturates to +inf, never NaN; keys below
+ *                                   are unaffected.
  *  window >= 0, eps >= 0
  *  target [B,Hkv,S] fp32 (SUM, MAX) or [B,Hq,S] fp32 (NONE)  output
  *  workspace, ws_bytes             >= kvpop_workspace_size(KVPOP_CALL_FUTURE_TARGET, ...)
@@ -170,7 +175,8 @@ kvpop_status kvpop_future_target_noalloc(const kvpop_shape *shape, const void *q
  *                                   element size < 2^31 bytes, else KVPOP_EUNSUPPORTED)
  *  scores [B,Hkv,S] fp32            static priorities
  *  sinks, window, topk >= 0
- *  o [B,Hq,S,D] (dtype), lse [B,Hq,S] fp32   outputs
+ *  o [B,Hq,S,D] (dtype), lse [B,Hq,S] fp32   outputs; both NULL: the mask alone (ranks,
+ *                                   cutoffs and the key lists in the workspace), no attention
  *  rank_out [B,Hkv,S] int32         optional (NULL): rank(t), a permutation of 0..S-1
  *  cutoff_out [B,Hkv,S] int32       optional (NULL): c_d, or KVPOP_CUTOFF_ALL
  *                                   when |E_d| < topk, or KVPOP_CUTOFF_NONE

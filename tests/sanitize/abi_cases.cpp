@@ -223,6 +223,12 @@ static void budget_cases() {
   expect("gather offsets above 2^31 bytes", bud(&big), KVPOP_EUNSUPPORTED);
   expect("budget null q", kvpop_budget_mask_fwd(&s, nullptr, P(), P(), F(), 1, 2, 3, P(), F(), nullptr, nullptr, P(),
                                                 kStubWorkspace, nullptr), KVPOP_EINVAL);
+  expect("budget mask alone", kvpop_budget_mask_fwd(&s, P(), P(), P(), F(), 1, 2, 3, nullptr, nullptr, I(), I(), P(),
+                                                  kStubWorkspace, nullptr), KVPOP_OK);
+  expect("budget null o only", kvpop_budget_mask_fwd(&s, P(), P(), P(), F(), 1, 2, 3, nullptr, F(), I(), I(), P(),
+                                                     kStubWorkspace, nullptr), KVPOP_EINVAL);
+  expect("budget null lse only", kvpop_budget_mask_fwd(&s, P(), P(), P(), F(), 1, 2, 3, P(), nullptr, I(), I(), P(),
+                                                       kStubWorkspace, nullptr), KVPOP_EINVAL);
   expect("budget null scores", kvpop_budget_mask_fwd(&s, P(), P(), P(), nullptr, 1, 2, 3, P(), F(), nullptr, nullptr,
                                                      P(), kStubWorkspace, nullptr), KVPOP_EINVAL);
   kvpop_lists_layout lay;

@@ -302,3 +302,25 @@ def test_budget_packed16k(kvpop_lib):
     say("budget packed16k docs", synth.doc_lengths_of(t["cu_seqlens"], 16384))
     check_budget(kvpop_lib, t["q"], t["k"], t["v"], sc, 4, 128, 1916, heads=[(0, g_) for g_ in range(32)],
                  rows=rows, cu=cu)
+
+
+def test_budget_mask_alone(kvpop_lib):
+    """With no outputs the call builds the mask alone: the same ranks,
+    cutoffs, list status and key lists as the whole call, packed or not."""
+    kv = kvpop_lib
+    for cu in (None, [0, 700, 1000, 2000]):
+        t = synth.make_qkv(1, 2000, 8, 2, 128, "bf16", 71, device=DEV, with_scores=True)
+        q, k, v, sc = t["q"], t["k"], t["v"], t["scores"]
+        cu_t = None if cu is None else torch.tensor(cu, dtype=torch.int32)
+        need = kv.workspace_size(kv.CALL_BUDGET_MASK_FWD, q, k, cu_seqlens=cu_t, sinks=4, window=64, topk=300)
+        ws1 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+        ws2 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+        _, _, r1, c1 = kv.budget_mask_fwd(q, k, v, sc, 4, 64, 300, workspace=ws1, cu_seqlens=cu_t)
+        o2, l2, r2, c2 = kv.budget_mask_fwd(q, k, v, sc, 4, 64, 300, workspace=ws2, cu_seqlens=cu_t,
+                                            need_output=False)
+        torch.cuda.synchronize()
+        assert o2 is None and l2 is None
+        assert torch.equal(r1, r2) and torch.equal(c1, c2)
+        lay = kv.budget_lists_layout(q, k, 4, 64, 300, cu_seqlens=cu_t)
+        a, b = lay["lists_offset"], lay["status_offset"] + 4 * 2 * lay["n_query_blocks"]
+        assert torch.equal(ws1[a:b], ws2[a:b]), "lists differ"

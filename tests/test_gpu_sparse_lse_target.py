@@ -80,3 +80,66 @@ def test_sparse_lse_target_equals_dense_when_budget_covers_all(kvpop_lib):
     torch.cuda.synchronize()
     assert_lse_close(lse_sp, lse_dn.cpu().double().numpy(), what="sparse vs dense lse")
     assert_target_close(t_sp, t_dn.cpu().double().numpy(), what="sparse-lse vs dense-lse target")
+
+
+def test_target_with_sparse_lse_packed16k(kvpop_lib):
+    """The pages' training configuration at its own shape: S=16384 packed as
+    6 documents, 32q/8kv/128, budget s=4, w=128, k=1916 (B=2048); the GPU
+    chains budget forward -> sparse LSE -> target (per query head and summed
+    over the group); the oracle's masked attention and transposed Eq. 8 with
+    its own L~ on KV heads 1 and 6 (8 query heads)."""
+    t = synth.make_workload("packed16k", device=DEV)
+    q, k, v, w = t["q"], t["k"], t["v"], t["window"]
+    cu_t = t["cu_seqlens"]
+    cu = cu_t.tolist()
+    g = torch.Generator(device=DEV).manual_seed(160)
+    sc = torch.randn(1, 8, 16384, generator=g, device=DEV)
+    s, kk = 4, 2048 - 4 - w
+    _, lse_sp, _, _ = kvpop_lib.budget_mask_fwd(q, k, v, sc, s, w, kk, return_rank_cutoff=False, cu_seqlens=cu_t)
+    tg = kvpop_lib.future_target(q, k, lse_sp, w, agg="none", cu_seqlens=cu_t)
+    tg_sum = kvpop_lib.future_target(q, k, lse_sp, w, agg="sum", cu_seqlens=cu_t)
+    torch.cuda.synchronize()
+    heads = [(0, g_) for g_ in list(range(4, 8)) + list(range(24, 28))]
+    gs = [g_ for _, g_ in heads]
+    say("packed16k sparse-LSE target: oracle")
+    q64, k64 = dense.to_f64(q), dense.to_f64(k)
+    r_rank, r_cut = budget.budget_reference(sc.cpu().numpy(), s, w, kk, cu=cu)
+    _, r_lse = budget.masked_attention(q64, k64, np.zeros_like(k64), r_rank, r_cut, s, w, heads=heads, cu=cu)
+    r_tl = dense.transposed_lse(q64, k64, r_lse, cu=cu, window=w, heads=heads)
+    e1 = assert_lse_close(lse_sp[:, gs], r_lse[:, gs], what="sparse lse")
+    e2 = assert_target_close(tg[:, gs], r_tl[:, gs], what="target with sparse lse, per query head")
+    with np.errstate(divide="ignore"):
+        r_sum = np.log(np.exp(r_tl[:, gs]).reshape(1, 2, 4, 16384).sum(axis=2))
+    e3 = assert_target_close(tg_sum[:, [1, 6]], r_sum, what="target with sparse lse, sum over the group")
+    say(f"packed16k sparse-LSE target: lse {e1:.2e} per head {e2:.2e} sum {e3:.2e}")
+
+
+def test_sparse_lse_target_saturates_to_inf(kvpop_lib):
+    """Beyond the stated precondition: an evicted key whose logit exceeds its
+    later queries' sparse normaliser by far more than 88 has a target above
+    ln(FLT_MAX) = 88.72; the kernel sums exp(s - L~) in fp32 without a
+    running maximum, so that key comes out +inf (documented saturation), never
+    NaN, while every key whose true target stays below 88 is within the
+    target tolerance (a second evicted key, at about 62, included)."""
+    S, Hq, Hkv, D = 1200, 4, 1, 128
+    lv = np.full(S, 0.1)
+    t_big, t_mid = 500, 800
+    lv[t_big] = 12.0      # logit ~136 against normalisers of ~6 over ~680 queries: target ~136
+    lv[t_mid] = 5.5       # logit ~62: target ~62
+    t = synth.make_leveled_qkv(S, Hq, Hkv, D, "bf16", 31, lv, device=DEV)
+    q, k, v = t["q"], t["k"], t["v"]
+    sc = torch.from_numpy(-lv).float().reshape(1, 1, S).to(DEV).contiguous()   # the spikes rank last
+    s, w, kk = 4, 16, 100
+    _, lse_sp, _, _ = kvpop_lib.budget_mask_fwd(q, k, v, sc, s, w, kk, return_rank_cutoff=False)
+    tg = kvpop_lib.future_target(q, k, lse_sp, w, agg="none")
+    torch.cuda.synchronize()
+    heads = [(0, g) for g in range(Hq)]
+    r_lse, r_tl = reference_target(q, k, sc, s, w, kk, heads)
+    assert_lse_close(lse_sp, r_lse, what="sparse lse")
+    g_ = tg.cpu().double().numpy()
+    assert not np.isnan(g_).any()
+    big = r_tl > 88.72 + 0.5
+    assert big.any() and np.all(np.isposinf(g_[big])), "keys above the fp32 range must saturate to +inf"
+    assert np.all(r_tl[:, :, t_mid] > 40)
+    ok = ~(r_tl > 88.0)
+    assert_target_close(g_[ok], r_tl[ok], what="target below the saturation")
