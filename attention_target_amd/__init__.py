@@ -58,7 +58,8 @@ class DecodeShape(ctypes.Structure):
 
 
 class ListsLayout(ctypes.Structure):
-    _fields_ = [("lists_offset", ctypes.c_size_t), ("lens_offset", ctypes.c_size_t),
+    _fields_ = [("lists_offset", ctypes.c_size_t), ("spans_offset", ctypes.c_size_t),
+                ("lens_offset", ctypes.c_size_t),
                 ("lens_full_offset", ctypes.c_size_t), ("status_offset", ctypes.c_size_t),
                 ("n_query_blocks", ctypes.c_int32), ("query_block", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("tile_keys", ctypes.c_int32)]

@@ -150,6 +150,7 @@ kvpop_status kvpop_budget_lists_layout(const kvpop_shape *shape, int32_t sinks, 
     return fail(KVPOP_EINVAL, "sinks, window and topk must be >= 0 (got %d, %d, %d)", sinks, window, topk);
   const kvpop::BudgetListsInfo li = kvpop::budget_lists_info(s, sinks, window, topk);
   layout->lists_offset = li.lists;
+  layout->spans_offset = li.spans;
   layout->lens_offset = li.lens;
   layout->lens_full_offset = li.lens_full;
   layout->status_offset = li.status;

@@ -5,7 +5,8 @@
 //         (the causal normaliser of the KVpop paper, Section 3.2).
 // Sparse: the same over the per-KV-head budget mask of Section 3 / 3.2
 //         (sinks, protected window, running top-k by static rank), reading
-//         only the keys listed for the query block.
+//         only the keys listed for the query block; each listed key carries
+//         the span [lo, hi) of query positions that keep it.
 //
 // Work decomposition: one workgroup = 4 waves = one block of QB query
 // positions x HG query heads of one KV head (HG = min(G, 4), QB = 32*4/HG), so
@@ -35,11 +36,10 @@ struct FwdParams {
   int n_docs;
   // budget-masked mode
   const int *lists;     // [B*Hkv][nqb][list_cap] key positions (two segments, see budget_lists)
+  const int2 *spans;    // [B*Hkv][nqb][list_cap]: per listed key, the queries [lo, hi) that keep it
   const int *list_len;       // [B*Hkv][nqb]
   const int *list_len_full;  // [B*Hkv][nqb]: leading entries kept by every query of the block
-  const int *rank;      // [B*Hkv][S]
-  const int *cutoff;    // [B*Hkv][S]
-  int list_cap, sinks, window;
+  int list_cap;
 };
 
 #ifndef KVPOP_FWD_KT
@@ -139,10 +139,7 @@ __device__ __forceinline__ void load_vt(Frag<float> &a, const char *vl, int j, i
   }
 }
 
-// SPARSE_DOCS: the budget-masked forward over packed documents (the element
-// mask also checks the document and counts sinks from its start); a separate
-// instantiation, so that single-document calls keep the shorter mask.
-template <typename T, int D, bool WITH_O, bool SPARSE, bool SPARSE_DOCS = false>
+template <typename T, int D, bool WITH_O, bool SPARSE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_FWD_WAVES))) attn_fwd_kernel(const FwdParams p) {
   using Tiles = FwdTiles<T, D>;
   using KTile = SwizzledTile<T, D>;
@@ -156,7 +153,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 
   // two stages of (K tile, V tile): one barrier per tile
   __shared__ __align__(16) char smem[2][Tiles::STAGE];
-  __shared__ __align__(16) int2 kpr_lds[2][KT];  // per listed key: (position, rank)
+  __shared__ __align__(16) int2 span_lds[2][KT];  // per listed key of a masked tile: its query span [lo, hi)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
@@ -188,7 +185,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   // Key range.
   int kbeg = 0, kend = 0, n_tiles = 0, list_len = 0, full_tiles = 0;
   const int *list = nullptr;
-  int wq_last = 0, wds_first = 0, wds_last = 0, qdoc_start = 0, cut_q = 0;
+  int wq_last = 0, wds_first = 0, wds_last = 0, qdoc_start = 0;
+  const int2 *spans = nullptr;
   if constexpr (!SPARSE) {
     const int blk_first = qb * QB;
     const int blk_last = min(p.S - 1, qb * QB + QB - 1);
@@ -205,8 +203,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
     list_len = min(p.list_len[tile_id], p.list_cap);
     n_tiles = (list_len + KT - 1) / KT;
     full_tiles = min(p.list_len_full[tile_id], list_len) / KT;
-    cut_q = p.cutoff[bh_kv * p.S + qc];
-    if constexpr (SPARSE_DOCS) qdoc_start = find_doc(p.cu, p.n_docs, p.S, qc).start;
+    spans = p.spans + tile_id * p.list_cap;
   }
 
   f32x16 o_acc[WITH_O ? NB : 1];
@@ -219,12 +216,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   const float c = p.scale_log2;
 
   // budget-masked path: the raw list entries of this lane's rows of the next
-  // tile's gathers (loaded one tile ahead), and of row `tid` for the mask.
-  // They are checked only when used, a tile later: checking them on arrival
-  // would wait on the list loads right away, and with them (loads complete
-  // in order) on the gathers issued just before.
+  // tile's gathers (loaded one tile ahead), and the query span of row `tid`
+  // for the mask.  They are checked only when used, a tile later: checking
+  // them on arrival would wait on the list loads right away, and with them
+  // (loads complete in order) on the gathers issued just before.
   int kraw[SPARSE ? LOADS : 1];
-  int next_raw = -1, my_kpos = INT32_MAX, my_krank = 0;
+  int2 next_span = make_int2(INT32_MAX, INT32_MAX);
   int vt_base[NB];  // per-lane part of the transposed V reads
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) vt_base[nb] = vt_off<ROWB>(lane, nb);
@@ -263,77 +260,55 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 
   // Gathered keys: the same direct-to-LDS loads, each lane's source row
   // taken from the list (positions loaded a tile earlier by load_keys).
-  // Rows past the list end get an offset beyond the buffer and arrive as
-  // zeros.  The buffers span the whole (batch, KV head) sequence.
-  // Per-lane constants of the gathers: the row of the tile each load serves
-  // and the swizzled chunk offsets of K and V in that row (the compiler keeps
-  // or recomputes them as registers allow).
-  int g_r[SPARSE ? LOADS : 1], g_ko[SPARSE ? LOADS : 1], g_vo[SPARSE ? LOADS : 1];
-  if constexpr (SPARSE) {
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const int pch = (wave * LOADS + k) * 64 + lane;
-      const int r = pch / CPR, slot = pch % CPR;
-      g_r[k] = r;
-      g_ko[k] = (slot ^ KTile::swz(r)) << 4;
-      g_vo[k] = (slot ^ Tiles::vswz(r)) << 4;
-    }
-  }
-  // The list entries of a tile come through a buffer resource over the
-  // block's list (entries past list_cap read as zero; every entry at or past
-  // list_len is rejected by entry() below).  The whole offset is in the
-  // per-lane register: the resource's range check does not cover the scalar
-  // offset.
+  // The buffers span the whole (batch, KV head) sequence.  Per-lane
+  // constants of the gathers, recomputed where used (a few integer
+  // operations; kept, they would hold six registers through the loop): the
+  // row of the tile a load serves and the swizzled chunk offsets of K and V
+  // in that row.
+  auto g_row = [&](int k) { return ((wave * LOADS + k) * 64 + lane) / CPR; };
+  auto g_koff = [&](int k) {
+    const int pch = (wave * LOADS + k) * 64 + lane;
+    return ((pch % CPR) ^ KTile::swz(pch / CPR)) << 4;
+  };
+  auto g_voff = [&](int k) {
+    const int pch = (wave * LOADS + k) * 64 + lane;
+    return ((pch % CPR) ^ Tiles::vswz(pch / CPR)) << 4;
+  };
+  // The list entries and spans of a tile come through buffer resources over
+  // the block's list, which the list builder pads to whole tiles with the
+  // row S (past the end of K and V: its loads return zeros) and a span that
+  // no query meets.  The whole offset is in the per-lane register: the
+  // resource's range check does not cover the scalar offset.
   auto load_keys = [&](int tile) {
     if constexpr (SPARSE) {
       const auto lr = make_rsrc(list, p.list_cap * 4);
 #pragma unroll
       for (int k = 0; k < LOADS; ++k)
-        kraw[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + g_r[k]) * 4, 0, 0);
-      if (tid < KT) next_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + tid) * 4, 0, 0);
+        kraw[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + g_row(k)) * 4, 0, 0);
+      if (tid < KT) {
+        const auto sr = make_rsrc(spans, p.list_cap * 8);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (tile * KT + tid) * 8, 0, 0);
+        next_span = make_int2((int)v[0], (int)v[1]);
+      }
     }
   };
-  // a list entry of tile `tile`, row r: its key position, or -1 past the
-  // list end or out of range
-  auto entry = [&](int raw, int tile, int r) {
-    const int lim = max(list_len - tile * KT, 0);  // rows of this tile inside the list
-    return ((unsigned)r < (unsigned)lim && (unsigned)raw < (unsigned)p.S) ? raw : -1;
-  };
+  // Entries are positions in [0, S] (S: padding).  Since S * ROWB < 2^31
+  // (checked on the host), the byte offset of an entry needs no clamp: any
+  // other value would fall outside the resource and read zeros as well.
   auto fetch_sparse = [&](int buf, int tile) {
     if constexpr (SPARSE) {
       const auto kr = make_rsrc(kbase, p.S * ROWB);
       const auto vr = make_rsrc(vbase, p.S * ROWB);
-      if (tile < full_tiles) {
-        // every row of an unmasked tile lies inside the list: only clamp
-        // the entry to S (row S starts at the buffer's end and reads zeros)
 #pragma unroll
-        for (int k = 0; k < LOADS; ++k) {
-          const int row = (int)min((unsigned)kraw[k], (unsigned)p.S) * ROWB;
-          lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
-          lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < LOADS; ++k) {
-          const int t = entry(kraw[k], tile, g_r[k]);
-          const int row = t >= 0 ? t * ROWB : 0x7fff0000;
-          lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_ko[k]);
-          lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_vo[k]);
-        }
+      for (int k = 0; k < LOADS; ++k) {
+        const int row = kraw[k] * ROWB;
+        lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_koff(k));
+        lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_voff(k));
       }
-      if (tid < KT && tile >= full_tiles) {
-        // positions and ranks are read only by masked tiles
-        const int t = entry(next_raw, tile, tid);
-        my_kpos = t >= 0 ? t : INT32_MAX;
-        my_krank = my_kpos != INT32_MAX ? p.rank[bh_kv * p.S + my_kpos] : INT32_MAX;
-      }
-    }
-  };
-  auto store_pos = [&](int buf) {
-    if constexpr (SPARSE) {
-      if (tid < KT) {
-        kpr_lds[buf][tid] = make_int2(my_kpos, my_krank);
-      }
+      // spans are read only by masked tiles.  The span was loaded a tile
+      // earlier and has arrived (the wait before this tile's barrier covers
+      // every load issued before).
+      if (tid < KT && tile >= full_tiles) span_lds[buf][tid] = next_span;
     }
   };
 
@@ -344,7 +319,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
     load_keys(0);
     if (n_tiles > 0) {
       fetch_sparse(0, 0);
-      if (0 >= full_tiles) store_pos(0);
       load_keys(1);
     }
   } else if (n_tiles > 0) {
@@ -401,12 +375,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               // the 4 rows of registers 4*i4 .. 4*i4+3 are adjacent: their
-              // (position, rank) pairs arrive in two 16-byte reads
+              // spans arrive in two 16-byte reads
               int4 pr[2];
               if constexpr (SPARSE) {
+                // one group of four rows at a time: read all at once, the
+                // spans would hold 32 registers through the masking
+                asm volatile("" ::: "memory");
                 const int r0 = 32 * rb + c_row(4 * i4, hf) + z;
-                pr[0] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0]);
-                pr[1] = *reinterpret_cast<const int4 *>(&kpr_lds[buf][r0 + 2]);
+                pr[0] = *reinterpret_cast<const int4 *>(&span_lds[buf][r0]);
+                pr[1] = *reinterpret_cast<const int4 *>(&span_lds[buf][r0 + 2]);
               }
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -416,16 +393,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
                   const int t = tb + 32 * rb + c_row(i, hf);
                   ok = qvalid && t <= qpos && t >= qdoc_start;
                 } else {
-                  const int t = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
-                  const int rk = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
-                  if constexpr (SPARSE_DOCS) {
-                    // same document, at or before the query, and a sink of
-                    // that document, in the window, or within the cutoff
-                    ok = qvalid && t <= qpos && t >= qdoc_start &&
-                         ((unsigned)(t - qdoc_start) < (unsigned)p.sinks || t > qpos - p.window || rk <= cut_q);
-                  } else {
-                    ok = qvalid && t <= qpos && (t < p.sinks || t > qpos - p.window || rk <= cut_q);
-                  }
+                  // the key's span of keeping queries
+                  const int lo = (e & 1) ? pr[e >> 1].z : pr[e >> 1].x;
+                  const int hi = (e & 1) ? pr[e >> 1].w : pr[e >> 1].y;
+                  ok = qvalid && qpos >= lo && qpos < hi;
                 }
                 s[rb][i] = ok ? s[rb][i] : -INFINITY;
               }
@@ -474,8 +445,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
       // maximum yet, the tile is redone against its exact masked maximum,
       // which also brings the running one to where later tiles pass again.
       float lt = 0.f;
-      bool exact = !started;
-      if (started) {
+      // Masked tiles of the budget-masked forward (a few per block) always
+      // take the exact path: one copy of the masking code instead of two.
+      constexpr bool FAST = FULL || !SPARSE;
+      bool exact = !FAST || !started;
+      if (FAST && started) {
         int z = 0;
         asm volatile("" : "+s"(z));
         logits(z);
@@ -527,9 +501,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
           }
         });
       }
-    }
-    if constexpr (SPARSE) {
-      if (tile + 1 < n_tiles && tile + 1 >= full_tiles) store_pos(buf ^ 1);
     }
 
   };

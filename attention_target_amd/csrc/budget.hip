@@ -37,7 +37,8 @@ constexpr int CUT_ALL = 2147483647;
 constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
-  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, lens, lens_full, lstatus, total;
+  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, spans, lens, lens_full, lstatus,
+      total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
 
@@ -54,9 +55,10 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   const int HG = fwd_heads_per_block(s.Hq / s.Hkv);
   lo.QB = 32 * (4 / HG);
   lo.nqb = (s.S + lo.QB - 1) / lo.QB;
+  // room for the longest list, padded to whole tiles of the attention kernel
   long long cap = (long long)sinks + topk + window + lo.QB;
   if (cap > s.S) cap = s.S;
-  lo.cap = (int)((cap + 3) & ~3ll);
+  lo.cap = (int)((cap + KVPOP_FWD_KT - 1) / KVPOP_FWD_KT * KVPOP_FWD_KT);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -74,6 +76,7 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   lo.prefix = take(BH * lo.L * lo.nw1 * 4);
   lo.zeros = take(BH * lo.L * 4);
   lo.lists = take(BH * lo.nqb * (size_t)lo.cap * 4);
+  lo.spans = take(BH * lo.nqb * (size_t)lo.cap * 8);
   lo.lens = take(BH * lo.nqb * 4);
   lo.lens_full = take(BH * lo.nqb * 4);
   lo.lstatus = take(BH * lo.nqb * 4);
@@ -89,6 +92,7 @@ BudgetListsInfo budget_lists_info(const ShapeInfo &s, int sinks, int window, int
   const BudgetLayout lo = budget_layout(s, sinks, window, topk);
   BudgetListsInfo li{};
   li.lists = lo.lists;
+  li.spans = lo.spans;
   li.lens = lo.lens;
   li.lens_full = lo.lens_full;
   li.status = lo.lstatus;
@@ -492,12 +496,22 @@ struct ListParams {
   const int *rank, *order, *cutoff;
   const int *cu;  // document offsets, or nullptr for one document per batch row
   int *lists, *lens, *lens_full, *status;
+  int2 *spans;
   int S, n_docs, sinks, window, topk, QB, nqb, cap;
 };
 
-// Key list of query block [d0, d1].  Within a document starting at a, query d
-// keeps the sinks [a, a+s), its window (d-w, d] and the eligible tokens of
+// Key list of query block [d0, d1].  Within a document [a, e), query d keeps
+// the sinks [a, a+s), its window (d-w, d] and the eligible tokens of
 // E_d = [a+s, d-w] with rank <= c_d.
+//
+// Every listed key t comes with the span [lo, hi) of query positions that
+// keep it, so that the attention kernel's element mask is lo <= d < hi.  The
+// queries keeping t form one interval: t itself onwards (causal); while t is
+// in their window (d < t + w) or a sink; then, once eligible, while
+// rank(t) <= c_d, which holds on a prefix since c_d does not rise; and never
+// past the document's end e.  So lo = t and hi is e for a sink, else the
+// first d >= t + w with c_d < rank(t), or e if no query of the block has
+// one (found by a binary search over the block's cutoffs).
 //
 // A block inside one document gets two segments:
 //   full:    the sinks below the window, the eligible tokens of [a+s, d0-w]
@@ -505,26 +519,28 @@ struct ListParams {
 //            of the block keeps all of them (c_d is non-increasing, so
 //            c_{d1} <= c_d; and (d1-w, d0] is inside every query's window
 //            and at or before every query), so their tiles need no
-//            per-element mask;
+//            per-element mask (their spans are the whole sequence);
 //   partial: the eligible tokens with c_{d1} < rank <= c_{d0}, then the
 //            rest of the window region (d0-w, d1]; these are masked per
-//            element.
+//            element with their spans.
 // The size of the full segment is known before the sweep: E_{d1} holds
 // exactly topk tokens of rank <= c_{d1}, so E_{d0} holds topk minus those in
 // (d0-w, d1-w] (at most QB-1 reads).
 // A block that spans documents lists, for each document's part [p0, p1],
 // the sinks below p0's window, the eligible tokens of E_{p0} with
 // rank <= c_{p0} and the positions (p0-w, p1] of the document, all in the
-// partial segment (the element mask also checks the document).  Only the
-// first part can reach back before d0, so the list still holds at most
+// partial segment (the spans end at the document's end).  Only the first
+// part can reach back before d0, so the list still holds at most
 // s + k + w + QB - 1 keys.
 // The eligible tokens are found by whichever sweep is shorter: over the
 // positions, or over the ranks [0, c] through the inverse permutation
 // (late blocks: c is about topk while the eligible range grows with d0).
 // The attention kernel needs no order inside a segment.
+constexpr int LIST_QB_MAX = 128;
 __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   __shared__ int sh_w[2][4];
   __shared__ int sh_sub;
+  __shared__ int sh_c[LIST_QB_MAX];  // c_d of the block's queries
   const int qb = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -533,13 +549,35 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   const int *ord = p.order + bh * p.S;
   const int *cut = p.cutoff + bh * p.S;
   int *list = p.lists + (bh * p.nqb + qb) * (size_t)p.cap;
+  int2 *span = p.spans + (bh * p.nqb + qb) * (size_t)p.cap;
+  if (tid < d1 - d0 + 1) sh_c[tid] = cut[d0 + tid];
+  __syncthreads();
   int off_f = 0, off_p = 0;
+  constexpr int EVERY = 0x7fffffff;  // span end of keys kept to the end of the sequence
+
+  // first query in [from, to] with c_d < r, else `none` (c_d does not rise
+  // inside one document, so the predicate holds on a suffix)
+  auto first_below = [&](int r, int from, int to, int none) {
+    if (from > to || sh_c[to - d0] >= r) return none;
+    int lo = from, hi = to;  // the answer lies in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sh_c[mid - d0] < r) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  // span of a non-sink key t of rank r whose document's queries in the block
+  // are [q0, q1] and whose document ends at e
+  auto span_of = [&](int t, int r, int q0, int q1, int e) {
+    return make_int2(t, first_below(r, max(q0, t + p.window), q1, e));
+  };
 
   // Appends the eligible tokens t in [lo, hi] with rank <= c_any: those with
-  // rank <= c_all at off_f (full segment), the others at off_p (partial).
-  // The loads of up to LIST_PF chunks of 256 go out before the first chunk
-  // is used (one memory round trip per LIST_PF chunks, not per chunk).
-  auto sweep = [&](int lo, int hi, int c_all, int c_any) {
+  // rank <= c_all at off_f (full segment), the others at off_p (partial, with
+  // their spans among the queries [q0, q1] of a document ending at e).  The
+  // loads of up to LIST_PF chunks of 256 go out before the first chunk is
+  // used (one memory round trip per LIST_PF chunks, not per chunk).
+  auto sweep = [&](int lo, int hi, int c_all, int c_any, int q0, int q1, int e) {
     const int n_pos = max(0, hi - lo + 1);
     if (n_pos == 0 || c_any == CUT_NONE) return;
     const bool by_rank = c_any != CUT_ALL && c_any + 1 < n_pos;
@@ -586,11 +624,17 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
         }
         if (ff) {
           const int slot = off_f + bf + __popcll(mf & lanemask_lt(lane));
-          if (slot < p.cap) list[slot] = t;
+          if (slot < p.cap) {
+            list[slot] = t;
+            span[slot] = make_int2(0, EVERY);
+          }
         }
         if (fp) {
           const int slot = off_p + bp + __popcll(mp & lanemask_lt(lane));
-          if (slot < p.cap) list[slot] = t;
+          if (slot < p.cap) {
+            list[slot] = t;
+            span[slot] = span_of(t, r, q0, q1, e);
+          }
         }
         off_f += tf;
         off_p += tp;
@@ -598,11 +642,13 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
       }
     }
   };
-  // positions [lo, lo + n) at off_p, skipping [skip_lo, skip_lo + n_skip)
-  auto append_range = [&](int lo, int n, int skip_lo, int n_skip) {
+  // positions [lo, lo + n) at off_p, skipping [skip_lo, skip_lo + n_skip),
+  // with their spans (sinks: kept to the document's end e)
+  auto append_range = [&](int lo, int n, int skip_lo, int n_skip, int e_lo, int q0, int q1, int e) {
     for (int i = tid; i < n && off_p + i < p.cap; i += 256) {
       const int t = (n_skip == 0 || lo + i < skip_lo) ? lo + i : lo + i + n_skip;
       list[off_p + i] = t;
+      span[off_p + i] = t < e_lo ? make_int2(t, e) : span_of(t, rk[t], q0, q1, e);
     }
     off_p += n;
   };
@@ -611,8 +657,8 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   int status = 0;
   if (d1 < doc0.end) {
     // the block lies inside one document
-    const int a = doc0.start, e_lo = a + p.sinks;
-    const int c0 = cut[d0], c1 = cut[d1];
+    const int a = doc0.start, e = doc0.end, e_lo = a + p.sinks;
+    const int c0 = sh_c[0], c1 = sh_c[d1 - d0];
     const int a_end = max(a, min(min(e_lo, d0 - p.window + 1), d1 + 1));  // sinks below the window: [a, a_end)
     const int n_a = a_end - a;
     const int b_hi = d0 - p.window;  // E_{d0} = [e_lo, b_hi]
@@ -639,29 +685,42 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
     const int wc_lo = max(c_lo, d1 - p.window + 1), wc_hi = d0;  // (d1-w, d0], possibly empty
     const int n_wc = max(0, wc_hi - wc_lo + 1);
     const int n_full = n_a + n_bfull + n_wc;
-    for (int i = tid; i < n_a && i < p.cap; i += 256) list[i] = a + i;
-    for (int i = tid; i < n_wc && n_a + n_bfull + i < p.cap; i += 256) list[n_a + n_bfull + i] = wc_lo + i;
+    for (int i = tid; i < n_a && i < p.cap; i += 256) {
+      list[i] = a + i;
+      span[i] = make_int2(0, EVERY);
+    }
+    for (int i = tid; i < n_wc && n_a + n_bfull + i < p.cap; i += 256) {
+      list[n_a + n_bfull + i] = wc_lo + i;
+      span[n_a + n_bfull + i] = make_int2(0, EVERY);
+    }
     off_f = n_a;
     off_p = n_full;
-    sweep(e_lo, b_hi, c1, c0);
+    sweep(e_lo, b_hi, c1, c0, d0, d1, e);
     if (off_f != n_a + n_bfull) status |= 2;
     // the masked part of R: all of R when (d1-w, d0] is empty, else
     // (d0-w, d1-w] then (d0, d1]
-    append_range(c_lo, d1 - c_lo + 1 - n_wc, wc_lo, n_wc);
+    append_range(c_lo, d1 - c_lo + 1 - n_wc, wc_lo, n_wc, e_lo, d0, d1, e);
     off_f += n_wc;
   } else {
     // the block spans documents: every part's keys are masked per element
     for (int m_lo = doc0.start; m_lo <= d1;) {
       const Doc dm = find_doc(p.cu, p.n_docs, p.S, m_lo);
-      const int a = dm.start, e_lo = a + p.sinks;
-      const int p0 = max(d0, a), p1 = min(d1, dm.end - 1);
+      const int a = dm.start, e = dm.end, e_lo = a + p.sinks;
+      const int p0 = max(d0, a), p1 = min(d1, e - 1);
       const int a_end = max(a, min(min(e_lo, p0 - p.window + 1), p1 + 1));
-      append_range(a, a_end - a, 0, 0);
-      sweep(e_lo, p0 - p.window, CUT_NONE, cut[p0]);
+      append_range(a, a_end - a, 0, 0, e_lo, p0, p1, e);
+      sweep(e_lo, p0 - p.window, CUT_NONE, sh_c[p0 - d0], p0, p1, e);
       const int c_lo = max(a, p0 - p.window + 1);
-      append_range(c_lo, max(0, p1 - c_lo + 1), 0, 0);
-      m_lo = dm.end;
+      append_range(c_lo, max(0, p1 - c_lo + 1), 0, 0, e_lo, p0, p1, e);
+      m_lo = e;
     }
+  }
+  // pad the list to whole tiles: position S (a row past the end of K and V,
+  // which the attention kernel's loads return as zeros) kept by no query
+  const int n_pad = (min(off_p, p.cap) + KVPOP_FWD_KT - 1) / KVPOP_FWD_KT * KVPOP_FWD_KT;
+  for (int i = min(off_p, p.cap) + tid; i < n_pad; i += 256) {
+    list[i] = p.S;
+    span[i] = make_int2(EVERY, EVERY);
   }
   if (tid == 0) {
     p.lens[bh * p.nqb + qb] = min(off_p, p.cap);
@@ -675,10 +734,7 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
 
 template <typename T, int D>
 static hipError_t run_sparse(const FwdParams &fp, int grid, hipStream_t st) {
-  if (fp.cu != nullptr)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true, true>), dim3(grid), dim3(256), 0, st, fp);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true, false>), dim3(grid), dim3(256), 0, st, fp);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, fp);
   return hipGetLastError();
 }
 
@@ -723,6 +779,7 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   lp.order = order;
   lp.cutoff = cutoff;
   lp.lists = reinterpret_cast<int *>(w + lo.lists);
+  lp.spans = reinterpret_cast<int2 *>(w + lo.spans);
   lp.lens = reinterpret_cast<int *>(w + lo.lens);
   lp.lens_full = reinterpret_cast<int *>(w + lo.lens_full);
   lp.status = reinterpret_cast<int *>(w + lo.lstatus);
@@ -755,13 +812,10 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   fp.cu = s.cu;
   fp.n_docs = s.n_docs;
   fp.lists = lp.lists;
+  fp.spans = lp.spans;
   fp.list_len = lp.lens;
   fp.list_len_full = lp.lens_full;
-  fp.rank = rank;
-  fp.cutoff = cutoff;
   fp.list_cap = lo.cap;
-  fp.sinks = sinks;
-  fp.window = window;
   const int grid = lo.nqb * s.B * s.Hkv * (fp.G / fp.HG);
   if (s.dtype == 0 && s.D == 128) return run_sparse<bf16, 128>(fp, grid, st);
   if (s.dtype == 0 && s.D == 64) return run_sparse<bf16, 64>(fp, grid, st);

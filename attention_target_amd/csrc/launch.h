@@ -42,7 +42,7 @@ size_t budget_workspace_bytes(const ShapeInfo &s, int sinks, int window, int top
 // Where kvpop_budget_mask_fwd leaves its per-query-block key lists in the
 // workspace (byte offsets) and how they are shaped.
 struct BudgetListsInfo {
-  size_t lists, lens, lens_full, status;
+  size_t lists, spans, lens, lens_full, status;
   int nqb, QB, cap, tile;
 };
 BudgetListsInfo budget_lists_info(const ShapeInfo &s, int sinks, int window, int topk);

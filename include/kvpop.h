@@ -199,7 +199,11 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
  *   int32 lists[i * capacity + j], j < lens[i]: the positions of the keys the
  *     block's queries may keep; the first lens_full[i] are kept by every
  *     query of the block, and whole tiles of tile_keys of them are attended
- *     without a per-element mask;
+ *     without a per-element mask; the list is padded to whole tiles with
+ *     position S;
+ *   int32 spans[2 * (i * capacity + j)], [... + 1]: lo and hi, the query
+ *     positions d with lo <= d < hi keep that key (the element mask of the
+ *     other tiles); padding keeps none;
  *   int32 lens[i], lens_full[i];
  *   int32 status[i]: 0 when the list is whole; bit 0 set when entries past
  *     the capacity were dropped; bit 1 set when the number of keys kept by
@@ -207,7 +211,7 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
  * Returns KVPOP_EINVAL for an invalid shape or negative budget parameters.
  */
 typedef struct {
-  size_t lists_offset, lens_offset, lens_full_offset, status_offset;
+  size_t lists_offset, spans_offset, lens_offset, lens_full_offset, status_offset;
   int32_t n_query_blocks, query_block, capacity, tile_keys;
 } kvpop_lists_layout;
 kvpop_status kvpop_budget_lists_layout(const kvpop_shape *shape, int32_t sinks, int32_t window,

@@ -50,6 +50,7 @@ size_t budget_workspace_bytes(const ShapeInfo &, int, int, int) { return kStubWo
 BudgetListsInfo budget_lists_info(const ShapeInfo &s, int sinks, int window, int topk) {
   BudgetListsInfo li{};
   li.lists = 256;
+  li.spans = 384;
   li.lens = 512;
   li.lens_full = 768;
   li.status = 1024;

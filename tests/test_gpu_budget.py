@@ -35,12 +35,17 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=None):
         covers the block's own positions whole; the mask drops them);
       * the shared segment (attended without a mask in whole tiles) is
         exactly the keys every query of the block keeps, outside the
-        positions (d0-w, d1-w], which are masked per query instead."""
+        positions (d0-w, d1-w], which are masked per query instead;
+      * every listed key's span [lo, hi) holds exactly the block's queries
+        whose mask row keeps it (the element mask of the masked tiles), and
+        the padding to whole tiles is position S, kept by no query."""
     lay = kv.budget_lists_layout(q, k, s, w, topk, cu_seqlens=cu)
     B, Hkv, S = r_rank.shape
     nqb, QB, cap = lay["n_query_blocks"], lay["query_block"], lay["capacity"]
     wsc = ws.cpu()
     lists = ws_int32(wsc, lay["lists_offset"], B * Hkv * nqb * cap).reshape(B * Hkv, nqb, cap)
+    spans = ws_int32(wsc, lay["spans_offset"], 2 * B * Hkv * nqb * cap).reshape(B * Hkv, nqb, cap, 2)
+    KT = lay["tile_keys"]
     lens = ws_int32(wsc, lay["lens_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
     lens_full = ws_int32(wsc, lay["lens_full_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
     status = ws_int32(wsc, lay["status_offset"], B * Hkv * nqb).reshape(B * Hkv, nqb)
@@ -62,6 +67,14 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=None):
             shared = rows.all(axis=0) & ((t <= d0 - w) | (t > d1 - w))
             full = lists[bh, qb, :lens_full[bh, qb]]
             assert np.array_equal(np.sort(full), np.nonzero(shared)[0]), (bh, qb, "shared segment")
+            n = lens[bh, qb]
+            sp = spans[bh, qb, :n]
+            d = np.arange(d0, d1 + 1)[:, None]
+            by_span = (d >= sp[None, :, 0]) & (d < sp[None, :, 1])
+            assert np.array_equal(by_span, rows[:, lst]), (bh, qb, "spans")
+            n_pad = -(-n // KT) * KT
+            assert np.all(lists[bh, qb, n:n_pad] == S), (bh, qb, "padding")
+            assert np.all(spans[bh, qb, n:n_pad, 0] == 2 ** 31 - 1), (bh, qb, "padding spans")
 
 
 def check_budget(kv, q, k, v, scores, s, w, topk, heads=None, rows=None, cu=None):
