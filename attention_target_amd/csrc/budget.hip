@@ -554,6 +554,11 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   __syncthreads();
   int off_f = 0, off_p = 0;
   constexpr int EVERY = 0x7fffffff;  // span end of keys kept to the end of the sequence
+  // Spans are read only for the masked tiles: every tile of the partial
+  // segment, and the last tile of the full segment when the full segment
+  // ends inside it.  Full entries before span_from get none (the bulk of
+  // the list: writing them all would triple the list's bytes).
+  int span_from = 0;
 
   // first query in [from, to] with c_d < r, else `none` (c_d does not rise
   // inside one document, so the predicate holds on a suffix)
@@ -626,7 +631,7 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
           const int slot = off_f + bf + __popcll(mf & lanemask_lt(lane));
           if (slot < p.cap) {
             list[slot] = t;
-            span[slot] = make_int2(0, EVERY);
+            if (slot >= span_from) span[slot] = make_int2(0, EVERY);
           }
         }
         if (fp) {
@@ -685,13 +690,14 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
     const int wc_lo = max(c_lo, d1 - p.window + 1), wc_hi = d0;  // (d1-w, d0], possibly empty
     const int n_wc = max(0, wc_hi - wc_lo + 1);
     const int n_full = n_a + n_bfull + n_wc;
+    span_from = n_full / KVPOP_FWD_KT * KVPOP_FWD_KT;
     for (int i = tid; i < n_a && i < p.cap; i += 256) {
       list[i] = a + i;
-      span[i] = make_int2(0, EVERY);
+      if (i >= span_from) span[i] = make_int2(0, EVERY);
     }
     for (int i = tid; i < n_wc && n_a + n_bfull + i < p.cap; i += 256) {
       list[n_a + n_bfull + i] = wc_lo + i;
-      span[n_a + n_bfull + i] = make_int2(0, EVERY);
+      if (n_a + n_bfull + i >= span_from) span[n_a + n_bfull + i] = make_int2(0, EVERY);
     }
     off_f = n_a;
     off_p = n_full;

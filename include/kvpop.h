@@ -201,9 +201,10 @@ kvpop_status kvpop_budget_mask_fwd(const kvpop_shape *shape, const void *q, cons
  *     query of the block, and whole tiles of tile_keys of them are attended
  *     without a per-element mask; the list is padded to whole tiles with
  *     position S;
- *   int32 spans[2 * (i * capacity + j)], [... + 1]: lo and hi, the query
+ *   int32 spans[2 * (i * capacity + j)], [... + 1] for j from
+ *     (lens_full[i] / tile_keys) * tile_keys on: lo and hi, the query
  *     positions d with lo <= d < hi keep that key (the element mask of the
- *     other tiles); padding keeps none;
+ *     masked tiles); padding keeps none;
  *   int32 lens[i], lens_full[i];
  *   int32 status[i]: 0 when the list is whole; bit 0 set when entries past
  *     the capacity were dropped; bit 1 set when the number of keys kept by

@@ -36,9 +36,10 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=None):
       * the shared segment (attended without a mask in whole tiles) is
         exactly the keys every query of the block keeps, outside the
         positions (d0-w, d1-w], which are masked per query instead;
-      * every listed key's span [lo, hi) holds exactly the block's queries
-        whose mask row keeps it (the element mask of the masked tiles), and
-        the padding to whole tiles is position S, kept by no query."""
+      * the span [lo, hi) of every key in a masked tile (from the last
+        whole tile of the shared segment on) holds exactly the block's
+        queries whose mask row keeps it, and the padding to whole tiles is
+        position S, kept by no query."""
     lay = kv.budget_lists_layout(q, k, s, w, topk, cu_seqlens=cu)
     B, Hkv, S = r_rank.shape
     nqb, QB, cap = lay["n_query_blocks"], lay["query_block"], lay["capacity"]
@@ -68,10 +69,11 @@ def check_lists(kv, q, k, s, w, topk, ws, r_rank, r_cut, cu=None):
             full = lists[bh, qb, :lens_full[bh, qb]]
             assert np.array_equal(np.sort(full), np.nonzero(shared)[0]), (bh, qb, "shared segment")
             n = lens[bh, qb]
-            sp = spans[bh, qb, :n]
+            j0 = lens_full[bh, qb] // KT * KT
+            sp = spans[bh, qb, j0:n]
             d = np.arange(d0, d1 + 1)[:, None]
             by_span = (d >= sp[None, :, 0]) & (d < sp[None, :, 1])
-            assert np.array_equal(by_span, rows[:, lst]), (bh, qb, "spans")
+            assert np.array_equal(by_span, rows[:, lst[j0:]]), (bh, qb, "spans")
             n_pad = -(-n // KT) * KT
             assert np.all(lists[bh, qb, n:n_pad] == S), (bh, qb, "padding")
             assert np.all(spans[bh, qb, n:n_pad, 0] == 2 ** 31 - 1), (bh, qb, "padding spans")
