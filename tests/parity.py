@@ -24,6 +24,12 @@ TARGET_FLOOR = -30.0
 OUT_REL_TOL = 2e-2
 
 
+def report(what, quantity, value, bar):
+    """One line per check with its worst case against its bar; pytest shows
+    these for passing tests with -rP."""
+    print(f"[parity] {what}: {quantity} = {value:.3g} (bar {bar:g})", flush=True)
+
+
 def as_np(x):
     import torch
     if isinstance(x, torch.Tensor):
@@ -39,6 +45,7 @@ def assert_lse_close(gpu, ref, tol=LSE_TOL, what="lse"):
     fin = ~ninf
     assert np.all(np.isfinite(g[fin])), f"{what}: non-finite values"
     err = np.abs(g[fin] - r[fin]).max() if fin.any() else 0.0
+    report(what, "lse max |delta|", err, tol)
     assert err <= tol, f"{what}: max |delta| = {err:.3g} > {tol}"
     return err
 
@@ -53,6 +60,7 @@ def assert_target_close(gpu, ref, tol=TARGET_TOL, floor=TARGET_FLOOR, what="targ
     big = np.isfinite(r) & (r > floor)
     assert np.all(np.isfinite(g[big])), f"{what}: {(~np.isfinite(g[big])).sum()} non-empty keys are -inf"
     err = np.abs(g[big] - r[big]).max() if big.any() else 0.0
+    report(what, "target max |delta|", err, tol)
     assert err <= tol, f"{what}: max |delta| = {err:.3g} > {tol}"
     small = np.isfinite(r) & (r <= floor)
     if small.any():
@@ -71,6 +79,7 @@ def assert_out_bounded(gpu, ref, abs_ref, u=2.0 ** -8, what="out"):
     err = np.abs(g - r)
     bound = 2.0 * u * a + 1e-6
     worst = float((err / bound).max())
+    report(what, "out error / rounding bound", worst, 1.0)
     assert worst <= 1.0, f"{what}: error reaches {worst:.3g} of the bf16 rounding bound"
     return worst
 
@@ -102,6 +111,7 @@ def assert_out_close(gpu, ref, rel=OUT_REL_TOL, what="out", out_round=None):
     ratio = err[~zero] / rms[~zero]
     worst = float(ratio.max()) if ratio.size else 0.0
     i = int(np.argmax(ratio)) if ratio.size else 0
+    report(what, "out row error / row RMS", worst, rel)
     assert worst <= rel, (f"{what}: row max |delta| / row RMS = {worst:.3g} > {rel} "
                           f"(row {i}: err {err[~zero][i]:.3g}, rms {rms[~zero][i]:.3g})")
     return worst
