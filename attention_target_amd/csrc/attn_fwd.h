@@ -59,6 +59,7 @@ struct FwdTiles {
   static constexpr int STAGE = 2 * K_BYTES;               // K tile, then V tile
   static constexpr int LOADS = K_BYTES / 4096;            // 1 KB direct loads per wave and tensor
   static_assert(KT * CPR % 256 == 0 && K_BYTES % 4096 == 0, "tile must split evenly over 4 waves");
+  static_assert(KT % 32 == 0, "a masked tile's spans load in 256-byte pieces");
   // V rows keep their natural layout; 16-byte chunk c of row r sits at slot
   // c ^ vswz(r), so that the transposed 8-byte reads of four consecutive
   // rows (or two rows of the other bank half, for 128-byte rows) hit
@@ -216,12 +217,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   const float c = p.scale_log2;
 
   // budget-masked path: the raw list entries of this lane's rows of the next
-  // tile's gathers (loaded one tile ahead), and the query span of row `tid`
-  // for the mask.  They are checked only when used, a tile later: checking
-  // them on arrival would wait on the list loads right away, and with them
-  // (loads complete in order) on the gathers issued just before.
+  // tile's gathers (loaded one tile ahead).  They are checked only when
+  // used, a tile later: checking them on arrival would wait on the list
+  // loads right away, and with them (loads complete in order) on the
+  // gathers issued just before.
   int kraw[SPARSE ? LOADS : 1];
-  int2 next_span = make_int2(INT32_MAX, INT32_MAX);
   int vt_base[NB];  // per-lane part of the transposed V reads
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) vt_base[nb] = vt_off<ROWB>(lane, nb);
@@ -285,11 +285,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
 #pragma unroll
       for (int k = 0; k < LOADS; ++k)
         kraw[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(lr, (tile * KT + g_row(k)) * 4, 0, 0);
-      if (tid < KT) {
-        const auto sr = make_rsrc(spans, p.list_cap * 8);
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (tile * KT + tid) * 8, 0, 0);
-        next_span = make_int2((int)v[0], (int)v[1]);
-      }
     }
   };
   // Entries are positions in [0, S] (S: padding).  Since S * ROWB < 2^31
@@ -305,10 +300,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
         lds_load16(kr, smem[buf] + (wave * LOADS + k) * 1024, row + g_koff(k));
         lds_load16(vr, smem[buf] + Tiles::K_BYTES + (wave * LOADS + k) * 1024, row + g_voff(k));
       }
-      // spans are read only by masked tiles.  The span was loaded a tile
-      // earlier and has arrived (the wait before this tile's barrier covers
-      // every load issued before).
-      if (tid < KT && tile >= full_tiles) span_lds[buf][tid] = next_span;
+      // Spans are read only by masked tiles, and go straight to LDS with the
+      // tile's rows: KT x 8 bytes in 4-byte pieces, 64 per load of wave 0.
+      // (Held in a register from a tile ahead instead, the span was spilled
+      // across the masked tiles' compute, and its reload waited for every
+      // gather in flight.)
+      if (wave == 0 && tile >= full_tiles) {
+        const auto sr = make_rsrc(spans, p.list_cap * 8);
+#pragma unroll
+        for (int i = 0; i < KT * 8 / 256; ++i)
+          lds_load4(sr, &span_lds[buf][32 * i], (tile * KT + 32 * i) * 8 + lane * 4);
+      }
     }
   };
 
