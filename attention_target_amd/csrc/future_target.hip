@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(256) future_target_finalize(const FinParams p)
 // host side
 
 int tgt_chunk(int max_doc) {
-  if (max_doc <= 4096) return 256;
+  if (max_doc <= 4096) return 192;
   if (max_doc <= 8192) return 512;
   return 1024;
 }
