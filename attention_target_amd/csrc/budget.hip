@@ -12,19 +12,20 @@
 // for all d in parallel.
 //
 // Pipeline (all on the caller's stream):
-//   1. keys:    64-bit sort key (descending score, ascending index) per token;
-//   2. sort:    2048-key chunks sorted in LDS (bitonic);
-//   3. rank:    rank(t) = sum over chunks of the number of smaller keys;
-//   4. wavelet: one workgroup per (batch, KV head) builds the log2(S) levels
+//   1. sort:    2048-key chunks sorted in LDS (bitonic), on 64-bit sort keys
+//               (descending score, ascending index) formed from the scores;
+//   2. rank:    rank(t) = sum over chunks of the number of smaller keys, and
+//               its inverse order[rank(t)] = t;
+//   3. wavelet: one workgroup per (batch, KV head) builds the log2(S) levels
 //               (bitvectors + per-word prefix counts) by stable partitions,
 //               inside LDS when the eligible range fits (32768 tokens);
-//   5. cutoff:  c_d for every d (KVPOP_CUTOFF_ALL when |E_d| < k, _NONE when
+//   4. cutoff:  c_d for every d (KVPOP_CUTOFF_ALL when |E_d| < k, _NONE when
 //               k = 0);
-//   6. lists:   per query block [d0, d1] the union of the keys any of its
+//   5. lists:   per query block [d0, d1] the union of the keys any of its
 //               queries may keep: [0, s) below the window, the eligible
 //               tokens of [s, d0-w] with rank <= c_{d0}, and (d0-w, d1], with
 //               the keys that every query of the block keeps listed first;
-//   7. forward: attention over the listed keys; tiles of the shared part
+//   6. forward: attention over the listed keys; tiles of the shared part
 //               need no mask, the rest use the per-element membership
 //               t <= d and (t < s or t > d-w or rank(t) <= c_d).
 #include "attn_fwd.h"
@@ -37,7 +38,7 @@ constexpr int CUT_ALL = 2147483647;
 constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
-  size_t keys, sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, spans, lens, lens_full, lstatus,
+  size_t sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, spans, lens, lens_full, lstatus,
       total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
@@ -65,7 +66,6 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
     off = al256(off + bytes);
     return o;
   };
-  lo.keys = take(BH * lo.S_pad * 8);
   lo.sorted = take(BH * lo.S_pad * 8);
   lo.rank = take(BH * s.S * 4);
   lo.order = take(BH * s.S * 4);
@@ -117,22 +117,30 @@ __device__ __forceinline__ uint64_t score_key(float sc, int t) {
   return ((uint64_t)(~ord) << 32) | (uint32_t)t;
 }
 
-__global__ void __launch_bounds__(256) budget_keys(const float *scores, uint64_t *keys, int S, int S_pad) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const size_t bh = blockIdx.y;
-  if (t >= S_pad) return;
-  keys[bh * S_pad + t] = (t < S) ? score_key(scores[bh * S + t], t) : ~0ull;
+// The sort key of position t of sequence bh (t < S_pad): formed from the
+// scores (the budget mask), or read from a key array (the teacher, whose keys
+// come from its own priorities).  Positions past S sort last.
+template <bool FROM_SCORES>
+__device__ __forceinline__ uint64_t key_at(const void *src, size_t bh, int t, int S, int S_pad) {
+  if constexpr (FROM_SCORES) {
+    return (t < S) ? score_key(reinterpret_cast<const float *>(src)[bh * S + t], t) : ~0ull;
+  } else {
+    return reinterpret_cast<const uint64_t *>(src)[bh * S_pad + t];
+  }
 }
 
 // Bitonic sort of one 2048-key chunk in LDS; 1024 threads, so every stage
 // is one compare-exchange per thread.
-__global__ void __launch_bounds__(1024) budget_sort_chunks(const uint64_t *keys, uint64_t *sorted, int S_pad) {
+template <bool FROM_SCORES>
+__global__ void __launch_bounds__(1024) budget_sort_chunks(const void *src, uint64_t *sorted, int S, int S_pad) {
   static_assert(RANK_CH == 2048, "one compare-exchange per thread and stage");
   __shared__ uint64_t sh[RANK_CH];
-  const size_t base = (size_t)blockIdx.y * S_pad + (size_t)blockIdx.x * RANK_CH;
+  const size_t bh = blockIdx.y;
+  const int t0 = (int)blockIdx.x * RANK_CH;
+  const size_t base = bh * S_pad + t0;
   const int tid = threadIdx.x;
-  sh[tid] = keys[base + tid];
-  sh[tid + 1024] = keys[base + tid + 1024];
+  sh[tid] = key_at<FROM_SCORES>(src, bh, t0 + tid, S, S_pad);
+  sh[tid + 1024] = key_at<FROM_SCORES>(src, bh, t0 + tid + 1024, S, S_pad);
   __syncthreads();
   for (int k = 2; k <= RANK_CH; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -151,19 +159,21 @@ __global__ void __launch_bounds__(1024) budget_sort_chunks(const uint64_t *keys,
   sorted[base + tid + 1024] = sh[tid + 1024];
 }
 
-// rank(t) = the number of keys below key(t), summed over the sorted chunks.
-// A workgroup ranks 256 tokens: it stages one sorted chunk at a time in LDS
-// (coalesced, double-buffered, the next chunk's loads in flight during the
-// current search) and each thread runs a branch-free lower-bound search of
-// fixed depth there, instead of scattered probes through L2.
-__global__ void __launch_bounds__(256) budget_rank(const uint64_t *keys, const uint64_t *sorted, int *rank,
+// rank(t) = the number of keys below key(t), summed over the sorted chunks,
+// and its inverse, order[rank(t)] = t.  A workgroup ranks 256 tokens: it
+// stages one sorted chunk at a time in LDS (coalesced, double-buffered, the
+// next chunk's loads in flight during the current search) and each thread
+// runs a branch-free lower-bound search of fixed depth there, instead of
+// scattered probes through L2.
+template <bool FROM_SCORES>
+__global__ void __launch_bounds__(256) budget_rank(const void *src, const uint64_t *sorted, int *rank, int *order,
                                                    int S, int S_pad, int nchunks) {
   __shared__ uint64_t ch[2][RANK_CH];
   constexpr int PER = RANK_CH / 256;
   const int tid = threadIdx.x;
   const int t = blockIdx.x * 256 + tid;
   const size_t bh = blockIdx.y;
-  const uint64_t key = keys[bh * S_pad + min(t, S_pad - 1)];
+  const uint64_t key = key_at<FROM_SCORES>(src, bh, min(t, S_pad - 1), S, S_pad);
   const uint64_t *srt = sorted + bh * S_pad;
   uint64_t stage[PER];
 #pragma unroll
@@ -186,7 +196,10 @@ __global__ void __launch_bounds__(256) budget_rank(const uint64_t *keys, const u
     // the buffer written next iteration is the other one; a barrier there
     // (after its writes) orders them against this iteration's reads of it
   }
-  if (t < S) rank[bh * S + t] = cnt;
+  if (t < S) {
+    rank[bh * S + t] = cnt;
+    if (cnt < S) order[bh * S + cnt] = t;  // keys are distinct: a permutation of [0, S)
+  }
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads).
@@ -483,15 +496,6 @@ __global__ void __launch_bounds__(256) budget_cutoffs(const WaveletParams p, con
   cutoff[bh * p.S + d] = res;
 }
 
-// Inverse of the rank permutation: order[r] = the token of rank r.
-__global__ void __launch_bounds__(256) rank_order(const int *rank, int *order, int S) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const size_t bh = blockIdx.y;
-  if (t >= S) return;
-  const int r = rank[bh * S + t];
-  if (r >= 0 && r < S) order[bh * S + r] = t;
-}
-
 struct ListParams {
   const int *rank, *order, *cutoff;
   const int *cu;  // document offsets, or nullptr for one document per batch row
@@ -750,14 +754,14 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   const BudgetLayout lo = budget_layout(s, sinks, window, topk);
   char *w = reinterpret_cast<char *>(ws);
   const int BH = s.B * s.Hkv;
-  uint64_t *keys = reinterpret_cast<uint64_t *>(w + lo.keys);
   uint64_t *sorted = reinterpret_cast<uint64_t *>(w + lo.sorted);
   int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
   int *cutoff = cutoff_out ? cutoff_out : reinterpret_cast<int *>(w + lo.cutoff);
 
-  hipLaunchKernelGGL(budget_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, scores, keys, s.S, lo.S_pad);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad);
-  hipLaunchKernelGGL(budget_rank, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, s.S, lo.S_pad, lo.nchunks);
+  int *order = reinterpret_cast<int *>(w + lo.order);
+  hipLaunchKernelGGL(budget_sort_chunks<true>, dim3(lo.nchunks, BH), dim3(1024), 0, st, scores, sorted, s.S, lo.S_pad);
+  hipLaunchKernelGGL(budget_rank<true>, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, scores, sorted, rank, order, s.S,
+                     lo.S_pad, lo.nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -778,8 +782,6 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  int *order = reinterpret_cast<int *>(w + lo.order);
-  hipLaunchKernelGGL(rank_order, dim3((s.S + 255) / 256, BH), dim3(256), 0, st, rank, order, s.S);
   ListParams lp{};
   lp.rank = rank;
   lp.order = order;
@@ -927,9 +929,9 @@ hipError_t launch_teacher(int B, int Hkv, int S, const float *y, const float *la
   int *rank = rank_out ? rank_out : reinterpret_cast<int *>(w + lo.rank);
   int *order = reinterpret_cast<int *>(w + lo.order);
   hipLaunchKernelGGL(teacher_keys, dim3(lo.S_pad / 256, BH), dim3(256), 0, st, y, lam, delta, keys, S, lo.S_pad, Hkv);
-  hipLaunchKernelGGL(budget_sort_chunks, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, lo.S_pad);
-  hipLaunchKernelGGL(budget_rank, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, S, lo.S_pad, lo.nchunks);
-  hipLaunchKernelGGL(rank_order, dim3((S + 255) / 256, BH), dim3(256), 0, st, rank, order, S);
+  hipLaunchKernelGGL(budget_sort_chunks<false>, dim3(lo.nchunks, BH), dim3(1024), 0, st, keys, sorted, S, lo.S_pad);
+  hipLaunchKernelGGL(budget_rank<false>, dim3((S + 255) / 256, BH), dim3(256), 0, st, keys, sorted, rank, order, S,
+                     lo.S_pad, lo.nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TeacherParams tp{};
