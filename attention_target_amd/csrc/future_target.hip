@@ -367,9 +367,20 @@ __global__ void __launch_bounds__(256) future_target_finalize(const FinParams p)
   const int nch = (n + p.DT - 1) / p.DT;
   const int jlo = (fq <= n - 1) ? fq / p.DT : nch;
   const float scale = p.mean ? (N > 0 ? 1.f / (float)N : 0.f) : 1.f;
+  // the chunks are added in index order; their loads are issued eight at a
+  // time (one after the other, each add would wait for its own load)
   auto mass = [&](int hp) {
+    const float *pp = p.part + ((size_t)b * p.Hp + hp) * p.nch_max * (size_t)p.S + t;
     float s = 0.f;
-    for (int jj = jlo; jj < nch; ++jj) s += p.part[(((size_t)b * p.Hp + hp) * p.nch_max + jj) * p.S + t];
+    int jj = jlo;
+    for (; jj + 8 <= nch; jj += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pp[(size_t)(jj + u) * p.S];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; jj < nch; ++jj) s += pp[(size_t)jj * p.S];
     return s * scale;
   };
   float y;
