@@ -116,6 +116,8 @@ SMALL = [
     (333, 4, 1, 64, "f32", 2, 9, 20, "normal"),
     (2500, 4, 1, 128, "bf16", 4, 128, 300, "decreasing"),
     (2500, 4, 1, 128, "bf16", 4, 128, 300, "increasing"),
+    (640, 6, 2, 128, "bf16", 4, 32, 90, "normal"),     # G = 3: 128-query blocks, three per KV head
+    (520, 12, 2, 64, "bf16", 2, 16, 60, "ties"),       # G = 6: 64-query blocks, three per KV head
 ]
 
 

@@ -72,6 +72,8 @@ CASES = [
     (700, 6, 3, 128, "bf16", 5, 1),
     (333, 4, 1, 64, "f32", 2, 9),
     (1100, 4, 1, 128, "bf16", 2, 128),
+    (450, 6, 2, 128, "bf16", 2, 32),    # G = 3: one head per block, three blocks per KV head
+    (390, 12, 2, 64, "bf16", 1, 7),     # G = 6: two heads per block, three blocks per KV head
 ]
 
 
