@@ -389,6 +389,18 @@ def measured_traffic(kernel_key: str):
     return round(k["fetch_kib"] * 1024 * t["fetch_factor"] + k["write_kib"] * 1024 * t["write_factor"])
 
 
+def copy_reference(mib: int, dev):
+    """Profiling runs only: a plain device copy of `mib` MiB, the reference
+    reading that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    if mib <= 0:
+        return
+    src = torch.ones(mib * (1 << 18), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +415,9 @@ def main():
     ap.add_argument("--budget-only", type=int, default=0, metavar="CALLS",
                     help="profiling runs only: time CALLS calls of the S=32768 budget workload and print "
                          "that measurement alone (not the metric line)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="profiling runs only: the smaller workloads (tiny, qwen4k, packed16k) alone, "
+                         "not the metric line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path needs no collectives: "
@@ -418,6 +433,13 @@ def main():
     dev = torch.device("cuda:0")
     if args.budget_only > 0:
         print(json.dumps({"budget_path": budget_measurement(kv, synth, dev, reps=args.budget_only)}), flush=True)
+        return
+    if args.configs_only:
+        small = {"tiny": config_line(kv, synth, dev, "tiny", 1, reps=50),
+                 "qwen4k": config_line(kv, synth, dev, "qwen4k", 2),
+                 "packed16k": config_line(kv, synth, dev, "packed16k", 1)}
+        copy_reference(args.copy_mib, dev)
+        print(json.dumps({"configs": small}), flush=True)
         return
     spec = synth.WORKLOADS["stack36"]
     L, B, S, Hq, Hkv, D, w = spec.layers, spec.batch, spec.seqlen, spec.n_q_heads, spec.n_kv_heads, \
@@ -533,12 +555,7 @@ def main():
             "stack36": {"note": "the metric line itself (value, roofline, kernels, cpu_baseline)"},
             "budget32k": budget_kernel_measurement(kv, synth, dev),
         }
-    if args.copy_mib > 0:
-        src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_reference(args.copy_mib, dev)
     print(json.dumps(out), flush=True)
 
 
