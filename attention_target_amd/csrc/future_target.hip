@@ -36,6 +36,10 @@
 //  * Blocks are ordered (batch, KV head, document, chunk descending, key tile)
 //    and dealt out so that each XCD (one L2) receives a contiguous range:
 //    concurrently running blocks of an XCD share the same query chunk.
+//    When B*Hkv is a multiple of 8, every XCD receives whole sequences, and
+//    a table written before the launch orders its blocks by size, largest
+//    first (longest-processing-time order): the last round then holds the
+//    small blocks on the diagonal, not a full-size block started late.
 #include <mutex>
 #include <type_traits>
 
@@ -60,6 +64,8 @@ struct TgtParams {
   const int *cu;
   int n_docs;
   int DT, nch_max, blocks_per_seq, total_blocks, Hp, kt;
+  const unsigned long long *order;  // per-XCD block order (see TgtOrder), or nullptr
+  int sx;                           // sequences per XCD when `order` is set
 };
 
 // Number of key tiles of a document of length n that meet query chunk j.
@@ -74,11 +80,106 @@ __host__ __device__ __forceinline__ int tgt_blocks_in_doc(int n, int DT, int w, 
   for (int j = 0; j < nch; ++j) c += tgt_tiles_in_chunk(n, j, DT, w, KT);
   return c;
 }
+// Size of a block in 32-query halves: the rows of its chunk [cq0, cq1) from
+// the 32-aligned row where its first key's future begins (the rows its first
+// wave computes).
+__host__ __device__ __forceinline__ int tgt_block_halves(int cq0, int cq1, int first_future) {
+  const int qs = max(cq0, first_future);
+  return (cq1 - (cq0 + ((qs - cq0) & ~31)) + 31) / 32;
+}
+
+// Block order within an XCD.  Each XCD runs sx = B*Hkv/8 whole sequences,
+// sx * blocks_per_seq blocks, taken largest first: by size in halves
+// (descending), then by sequence, then in enumeration order (document,
+// chunk descending, key tile).  Sizes within one (document, chunk) group
+// never rise with the key tile, so blocks of one size are contiguous there.
+// Entry = tile | chunk << 16 | sequence << 32 | document << 48.  The table is
+// the same for every XCD and is written by the first workgroup of
+// future_target_neg_lse, which runs before the target kernel on the stream.
+constexpr int TGT_ORDER_MAX_GROUPS = 256;          // (document, chunk) groups per sequence
+constexpr int TGT_ORDER_CLASSES = 1024 / 32 + 1;   // sizes 1 .. DT/32 halves, DT <= 1024
+struct TgtOrder {
+  unsigned long long *order;  // [sx * blocks_per_seq], or nullptr: no table
+  const int *cu;
+  int n_docs, S, DT, window, KT, sx, n_groups;
+};
+
+__device__ void tgt_build_order(const TgtOrder &o) {
+  __shared__ unsigned short gm[TGT_ORDER_MAX_GROUPS], gj[TGT_ORDER_MAX_GROUPS];
+  // per size class and group: tiles of that size, then their exclusive
+  // prefix over the groups (each < 65536: a chunk has at most S/128 tiles)
+  __shared__ unsigned short cnt[TGT_ORDER_CLASSES][TGT_ORDER_MAX_GROUPS];
+  __shared__ int tot[TGT_ORDER_CLASSES];
+  __shared__ long long base[TGT_ORDER_CLASSES];
+  const int tid = threadIdx.x, ng = o.n_groups, nc = o.DT / 32 + 1;
+  if (tid == 0) {
+    int g = 0;
+    for (int m = 0; m < o.n_docs && g < ng; ++m) {
+      const int n = o.cu != nullptr ? o.cu[m + 1] - o.cu[m] : o.S;
+      for (int j = (n + o.DT - 1) / o.DT - 1; j >= 0 && g < ng; --j, ++g) {
+        gm[g] = (unsigned short)m;
+        gj[g] = (unsigned short)j;
+      }
+    }
+    for (; g < ng; ++g) gm[g] = 0xffff;  // device offsets disagree with the host's: no tiles
+  }
+  for (int i = tid; i < TGT_ORDER_CLASSES * TGT_ORDER_MAX_GROUPS; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  int n = 0, j = 0, cq0 = 0, cq1 = 0, nt = 0;
+  if (tid < ng && gm[tid] < o.n_docs) {
+    const int m = gm[tid];
+    n = o.cu != nullptr ? o.cu[m + 1] - o.cu[m] : o.S;
+    j = gj[tid];
+    cq0 = j * o.DT;
+    cq1 = min(n, cq0 + o.DT);
+    nt = tgt_tiles_in_chunk(n, j, o.DT, o.window, o.KT);
+    for (int r = 0; r < nt; ++r) ++cnt[tgt_block_halves(cq0, cq1, r * o.KT + o.window)][tid];
+  }
+  __syncthreads();
+  if (tid < nc) {
+    int a = 0;
+    for (int g = 0; g < ng; ++g) {
+      const int v = cnt[tid][g];
+      cnt[tid][g] = (unsigned short)a;
+      a += v;
+    }
+    tot[tid] = a;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long a = 0;
+    for (int c = nc - 1; c >= 0; --c) {
+      base[c] = a;
+      a += (long long)o.sx * tot[c];
+    }
+  }
+  __syncthreads();
+  if (tid < ng && nt > 0) {
+    const unsigned long long gbits = ((unsigned long long)j << 16) | ((unsigned long long)gm[tid] << 48);
+    int prev = -1, run0 = 0;
+    for (int r = 0; r < nt; ++r) {
+      const int c = tgt_block_halves(cq0, cq1, r * o.KT + o.window);
+      if (c != prev) {
+        prev = c;
+        run0 = r;
+      }
+      const long long at = base[c] + cnt[c][tid] + (r - run0);
+      for (int sq = 0; sq < o.sx; ++sq)
+        o.order[at + (long long)sq * tot[c]] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
+    }
+  }
+}
 
 // -L/scale for every query (mul = -1/scale): the MFMA addend of the target
-// kernel, in the units of the raw logits q.k.
-__global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, float *nl, float mul, size_t count) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+// kernel, in the units of the raw logits q.k.  With a block-order table to
+// write, the first workgroup writes it and the others shift by one.
+__global__ void __launch_bounds__(256) future_target_neg_lse(const float *lse, float *nl, float mul, size_t count,
+                                                             const TgtOrder o) {
+  if (o.order != nullptr && blockIdx.x == 0) {
+    tgt_build_order(o);
+    return;
+  }
+  const size_t i = (size_t)(blockIdx.x - (o.order != nullptr ? 1 : 0)) * 256 + threadIdx.x;
   if (i < count) nl[i] = lse[i] * mul;
 }
 
@@ -105,33 +206,50 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(tgt_wa
   const int per_xcd = (p.total_blocks + 7) / 8;
   const int v = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
   if (v >= p.total_blocks) return;
-  const int bh = v / p.blocks_per_seq;
-  int r = v % p.blocks_per_seq;
-  const int b = bh / p.Hkv, h = bh % p.Hkv;
-  int dstart = 0, n = p.S;
-  bool found = false;
-  for (int m = 0; m < p.n_docs; ++m) {
+  int bh, r, j, dstart = 0, n = p.S;
+  if (p.order != nullptr) {
+    // the grid is exactly 8 * sx * blocks_per_seq: entry blockIdx/8 of the table
+    const unsigned long long e = p.order[blockIdx.x / 8];
+    r = (int)(e & 0xffff);
+    j = (int)((e >> 16) & 0xffff);
+    const int sq = (int)((e >> 32) & 0xffff), m = (int)(e >> 48);
+    if (sq >= p.sx || m >= p.n_docs) return;
+    bh = ((int)blockIdx.x % 8) * p.sx + sq;
     if (p.cu != nullptr) {
       dstart = p.cu[m];
       n = p.cu[m + 1] - dstart;
     }
-    const int cnt = tgt_blocks_in_doc(n, p.DT, p.window, KT);
-    if (r < cnt) {
-      found = true;
-      break;
+    if (n <= 0 || dstart < 0 || dstart + n > p.S) return;  // host and device offsets disagree
+    const int nch = (n + p.DT - 1) / p.DT;
+    if (nch > p.nch_max || j >= nch || r >= tgt_tiles_in_chunk(n, j, p.DT, p.window, KT)) return;
+  } else {
+    bh = v / p.blocks_per_seq;
+    r = v % p.blocks_per_seq;
+    bool found = false;
+    for (int m = 0; m < p.n_docs; ++m) {
+      if (p.cu != nullptr) {
+        dstart = p.cu[m];
+        n = p.cu[m + 1] - dstart;
+      }
+      const int cnt = tgt_blocks_in_doc(n, p.DT, p.window, KT);
+      if (r < cnt) {
+        found = true;
+        break;
+      }
+      r -= cnt;
     }
-    r -= cnt;
+    if (!found || n <= 0 || dstart < 0 || dstart + n > p.S) return;  // host and device offsets disagree
+    const int nch = (n + p.DT - 1) / p.DT;
+    if (nch > p.nch_max) return;
+    j = nch - 1;
+    for (; j >= 0; --j) {
+      const int nt = tgt_tiles_in_chunk(n, j, p.DT, p.window, KT);
+      if (r < nt) break;
+      r -= nt;
+    }
+    if (j < 0) return;
   }
-  if (!found || n <= 0 || dstart < 0 || dstart + n > p.S) return;  // host and device offsets disagree
-  const int nch = (n + p.DT - 1) / p.DT;
-  if (nch > p.nch_max) return;
-  int j = nch - 1;
-  for (; j >= 0; --j) {
-    const int nt = tgt_tiles_in_chunk(n, j, p.DT, p.window, KT);
-    if (r < nt) break;
-    r -= nt;
-  }
-  if (j < 0) return;
+  const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int t0 = r * KT;  // doc-local first key of the block
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,20 +524,55 @@ int tgt_chunk(int max_doc) {
 
 // Workspace: per-chunk partial sums [B, Hp, n_chunks, S] (Hp = Hkv for the
 // SUM aggregation, which adds a group's query heads inside the kernel, else
-// Hq), then the normaliser in logit units -L/scale [B, Hq, S].  Every
-// partial the finalize step reads is written by the same call, so the
-// workspace needs no clearing.
+// Hq), then the normaliser in logit units -L/scale [B, Hq, S], then (at a
+// 256-byte boundary) the block-order table when one is used.  Every value
+// the kernels read is written by the same call, so the workspace needs no
+// clearing.
 static size_t tgt_partial_floats(const ShapeInfo &s, int Hp) {
   const int DT = tgt_chunk(s.max_doc);
   const size_t nch_max = (size_t)((s.max_doc + DT - 1) / DT);
   return (size_t)s.B * Hp * nch_max * s.S;
 }
 static int tgt_partial_heads(const ShapeInfo &s, int agg) { return agg == 0 ? s.Hkv : s.Hq; }
-size_t tgt_workspace_bytes(const ShapeInfo &s) {
-  return (tgt_partial_floats(s, s.Hq) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+// (document, chunk) groups of one sequence
+static long long tgt_groups(const ShapeInfo &s, int DT) {
+  if (s.cu_host == nullptr) return (s.S + DT - 1) / DT;
+  long long g = 0;
+  for (int m = 0; m < s.n_docs; ++m) g += (s.cu_host[m + 1] - s.cu_host[m] + DT - 1) / DT;
+  return g;
 }
+// Blocks of one sequence for any window and key tile (the most: w = 0,
+// 128-key tiles).
+static long long tgt_blocks_bound(const ShapeInfo &s) {
+  const int DT = tgt_chunk(s.max_doc);
+  long long per_seq = 0;
+  if (s.cu_host != nullptr) {
+    for (int m = 0; m < s.n_docs; ++m) per_seq += tgt_blocks_in_doc(s.cu_host[m + 1] - s.cu_host[m], DT, 0, tgt_kt<1>());
+  } else {
+    per_seq = tgt_blocks_in_doc(s.S, DT, 0, tgt_kt<1>());
+  }
+  return per_seq;
+}
+// Whether the blocks run in the size order of a table: every XCD must get
+// whole sequences, and the groups, the builder's 16-bit counts and the entry
+// fields must fit.
+static bool tgt_ordered(const ShapeInfo &s) {
+  const int DT = tgt_chunk(s.max_doc);
+  const long long nseq = (long long)s.B * s.Hkv;
+  return nseq % 8 == 0 && nseq / 8 < 65536 && s.n_docs < 65536 && (s.cu == nullptr) == (s.cu_host == nullptr) &&
+         tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536;
+}
+// Bytes of the table for any window and key tile, plus the alignment.
+static size_t tgt_order_bytes(const ShapeInfo &s) {
+  if (!tgt_ordered(s)) return 0;
+  return 256 + sizeof(unsigned long long) * (size_t)((long long)s.B * s.Hkv / 8) * (size_t)tgt_blocks_bound(s);
+}
+static size_t tgt_base_bytes(const ShapeInfo &s, int Hp) {
+  return (tgt_partial_floats(s, Hp) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+}
+size_t tgt_workspace_bytes(const ShapeInfo &s) { return tgt_base_bytes(s, s.Hq) + tgt_order_bytes(s); }
 size_t tgt_workspace_bytes_for(const ShapeInfo &s, int agg) {
-  return (tgt_partial_floats(s, tgt_partial_heads(s, agg)) + (size_t)s.B * s.Hq * s.S) * sizeof(float);
+  return tgt_base_bytes(s, tgt_partial_heads(s, agg)) + tgt_order_bytes(s);
 }
 
 // Scratch of the no-allocation entry point (kvpop_future_target_noalloc):
@@ -512,12 +665,27 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
   tp.total_blocks = (int)(per_seq * s.B * s.Hkv);
   const bool sum = (agg == 0);
   tp.Hp = tgt_partial_heads(s, agg);
+  TgtOrder ord{};
+  if (tgt_ordered(s)) {
+    const size_t off = (tgt_base_bytes(s, tp.Hp) + 255) & ~(size_t)255;
+    ord.order = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ws) + off);
+    ord.cu = s.cu;
+    ord.n_docs = s.n_docs;
+    ord.S = s.S;
+    ord.DT = tp.DT;
+    ord.window = window;
+    ord.KT = tp.kt;
+    ord.sx = s.B * s.Hkv / 8;
+    ord.n_groups = (int)tgt_groups(s, tp.DT);
+    tp.order = ord.order;
+    tp.sx = ord.sx;
+  }
   hipError_t e = hipSuccess;
   if (tp.total_blocks > 0) {
     const size_t count = (size_t)s.B * s.Hq * s.S;
     const float mul = (float)(-1.0 / (double)s.scale);
-    hipLaunchKernelGGL(future_target_neg_lse, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, lse, nl,
-                       mul, count);
+    const unsigned nl_blocks = (unsigned)((count + 255) / 256) + (ord.order != nullptr ? 1u : 0u);
+    hipLaunchKernelGGL(future_target_neg_lse, dim3(nl_blocks), dim3(256), 0, st, lse, nl, mul, count, ord);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int grid = 8 * ((tp.total_blocks + 7) / 8);
     if (s.dtype == 0 && s.D == 128) e = sum ? launch_tgt<bf16, 128, true>(tp, grid, st) : launch_tgt<bf16, 128, false>(tp, grid, st);

@@ -97,6 +97,43 @@ def test_random_shapes(kvpop_lib, S, Hq, Hkv, D, dt, docs, w):
     assert_target_close(tn, refn, what="target none")
 
 
+ORDER_CASES = [
+    # B, S, Hq, Hkv, D, docs, w: B*Hkv a multiple of 8, so each XCD runs whole
+    # sequences and the blocks run in the size order of the table (packed
+    # documents come with batch 1)
+    (1, 1500, 16, 8, 128, 3, 40),
+    (2, 900, 8, 4, 64, 1, 0),
+    (8, 300, 2, 1, 128, 1, 7),
+    (2, 700, 16, 8, 64, 1, 20),      # two sequences per XCD
+    (1, 5000, 8, 8, 64, 1, 128),     # 512-query chunks (documents up to 8192)
+    (1, 6000, 8, 8, 128, 3, 300),    # packed: 990, 4171 and 839 tokens (512-query chunks)
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,docs,w", ORDER_CASES)
+def test_target_block_order(kvpop_lib, B, S, Hq, Hkv, D, docs, w):
+    """Shapes whose target blocks run in the table's size order.  The
+    workspace starts as all-ones bytes (NaN partials, invalid table entries),
+    so a block that the table misses or repeats leaves a NaN or a wrong sum:
+    every aggregation is compared with the oracle."""
+    seed = 1000 + S + B + docs
+    say(f"block order B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} docs={docs} w={w}")
+    t = synth.make_qkv(B, S, Hq, Hkv, D, "bf16", seed, device=DEV, heavy_hitters=True)
+    cu = synth.cu_seqlens_from_lengths(synth.doc_lengths(S, docs, 100, seed)) if docs > 1 else None
+    cl = cu.tolist() if cu is not None else None
+    q, k, v = t["q"], t["k"], t["v"]
+    r = oracle_ref(q, k, None, cl, w, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    need = kvpop_lib.workspace_size(kvpop_lib.CALL_FUTURE_TARGET, q, k, cu_seqlens=cu, window=w)
+    for agg, mean in [("sum", False), ("max", True), ("none", False)]:
+        ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+        tg = kvpop_lib.future_target(q, k, lse, w, agg=agg, mean_over_queries=mean, cu_seqlens=cu, workspace=ws)
+        torch.cuda.synchronize()
+        ref = dense.target_from_colmass(r["colmass"], Hkv, cl, w, AGG[agg], mean, 0.0)
+        e = assert_target_close(tg, ref, what=f"target[{agg}]")
+        say(f"  {agg} mean={mean}: target err {e:.2e}")
+
+
 @pytest.mark.parametrize("kind,docs", [("rising", 1), ("jumps", 1), ("jumps", 3), ("falling", 1),
                                        ("negative", 1), ("negative", 4)])
 def test_forward_running_maximum(kvpop_lib, kind, docs):
