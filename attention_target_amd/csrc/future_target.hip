@@ -93,6 +93,12 @@ __host__ __device__ __forceinline__ int tgt_block_halves(int cq0, int cq1, int f
 // (descending), then by sequence, then in enumeration order (document,
 // chunk descending, key tile).  Sizes within one (document, chunk) group
 // never rise with the key tile, so blocks of one size are contiguous there.
+// Sorting every block by size has a cost in memory traffic: each size class
+// spans all chunks, so the diagonal blocks re-read their queries from
+// memory instead of sharing them in L2 with the full blocks of their chunk
+// (the target's HBM bytes at S=16384 rise 1.6x, to about 0.65 TB/s, far from
+// the HBM roof).  Moving only the blocks of at most a quarter chunk to the
+// end kept the traffic but not the shorter last round.
 // Entry = tile | chunk << 16 | sequence << 32 | document << 48.  The table is
 // the same for every XCD and is written by the first workgroup of
 // future_target_neg_lse, which runs before the target kernel on the stream.
@@ -560,7 +566,7 @@ static bool tgt_ordered(const ShapeInfo &s) {
   const int DT = tgt_chunk(s.max_doc);
   const long long nseq = (long long)s.B * s.Hkv;
   return nseq % 8 == 0 && nseq / 8 < 65536 && s.n_docs < 65536 && (s.cu == nullptr) == (s.cu_host == nullptr) &&
-         tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536;
+         DT / 32 + 1 <= TGT_ORDER_CLASSES && tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536;
 }
 // Bytes of the table for any window and key tile, plus the alignment.
 static size_t tgt_order_bytes(const ShapeInfo &s) {
