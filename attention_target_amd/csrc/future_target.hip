@@ -105,73 +105,119 @@ __host__ __device__ __forceinline__ int tgt_block_halves(int cq0, int cq1, int f
 constexpr int TGT_ORDER_MAX_GROUPS = 256;          // (document, chunk) groups per sequence
 constexpr int TGT_ORDER_CLASSES = 1024 / 32 + 1;   // sizes 1 .. DT/32 halves, DT <= 1024
 struct TgtOrder {
-  unsigned long long *order;  // [sx * blocks_per_seq], or nullptr: no table
+  unsigned long long *order;  // [cap = sx * blocks_per_seq], or nullptr: no table
+  long long cap;              // entries; the builder writes none past it
   const int *cu;
   int n_docs, S, DT, window, KT, sx, n_groups;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// One workgroup of 256 threads; every phase is parallel (threads over
+// groups, waves over classes), so the table is ready in a few microseconds.
 __device__ void tgt_build_order(const TgtOrder &o) {
-  __shared__ unsigned short gm[TGT_ORDER_MAX_GROUPS], gj[TGT_ORDER_MAX_GROUPS];
+  __shared__ int dlen[TGT_ORDER_MAX_GROUPS], dgrp[TGT_ORDER_MAX_GROUPS];
   // per size class and group: tiles of that size, then their exclusive
-  // prefix over the groups (each < 65536: a chunk has at most S/128 tiles)
+  // prefix over the groups (each < 65536: the host bounds a sequence's blocks)
   __shared__ unsigned short cnt[TGT_ORDER_CLASSES][TGT_ORDER_MAX_GROUPS];
   __shared__ int tot[TGT_ORDER_CLASSES];
   __shared__ long long base[TGT_ORDER_CLASSES];
-  const int tid = threadIdx.x, ng = o.n_groups, nc = o.DT / 32 + 1;
-  if (tid == 0) {
-    int g = 0;
-    for (int m = 0; m < o.n_docs && g < ng; ++m) {
-      const int n = o.cu != nullptr ? o.cu[m + 1] - o.cu[m] : o.S;
-      for (int j = (n + o.DT - 1) / o.DT - 1; j >= 0 && g < ng; --j, ++g) {
-        gm[g] = (unsigned short)m;
-        gj[g] = (unsigned short)j;
-      }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ng = o.n_groups, nc = o.DT / 32 + 1;
+  // documents: lengths and their first group (groups run document by
+  // document, chunks descending)
+  if (tid < o.n_docs) dlen[tid] = o.cu != nullptr ? o.cu[tid + 1] - o.cu[tid] : o.S;
+  for (int i = tid; i < TGT_ORDER_CLASSES * TGT_ORDER_MAX_GROUPS; i += 256) (&cnt[0][0])[i] = 0;
+  if (wave == 0) {
+    // group offsets of documents 0..255, 64 at a time
+    int carry = 0;
+    for (int d0 = 0; d0 < o.n_docs; d0 += 64) {
+      const int d = d0 + lane;
+      const int v = d < o.n_docs ? (o.cu != nullptr ? o.cu[d + 1] - o.cu[d] : o.S) : 0;
+      const int c = v > 0 ? (v + o.DT - 1) / o.DT : 0;
+      const int inc = wave_incl_scan(c);
+      if (d < o.n_docs) dgrp[d] = carry + inc - c;
+      carry += __shfl(inc, 63);
     }
-    for (; g < ng; ++g) gm[g] = 0xffff;  // device offsets disagree with the host's: no tiles
   }
-  for (int i = tid; i < TGT_ORDER_CLASSES * TGT_ORDER_MAX_GROUPS; i += blockDim.x) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  int n = 0, j = 0, cq0 = 0, cq1 = 0, nt = 0;
-  if (tid < ng && gm[tid] < o.n_docs) {
-    const int m = gm[tid];
-    n = o.cu != nullptr ? o.cu[m + 1] - o.cu[m] : o.S;
-    j = gj[tid];
+  // this thread's group: document m (the last whose first group is <= tid)
+  // and chunk j, counting chunks down from the document's last
+  int m = -1, j = 0, cq0 = 0, cq1 = 0, nt = 0, nfull = 0, cf = 0;
+  if (tid < ng) {
+    for (int d = 0; d < o.n_docs; ++d)
+      if (dgrp[d] <= tid && dlen[d] > 0) m = d;
+  }
+  if (m >= 0) {
+    const int n = dlen[m];
+    j = (n + o.DT - 1) / o.DT - 1 - (tid - dgrp[m]);
+    if (j < 0) m = -1;  // device offsets disagree with the host's: no tiles
+  }
+  if (m >= 0) {
+    const int n = dlen[m];
     cq0 = j * o.DT;
     cq1 = min(n, cq0 + o.DT);
     nt = tgt_tiles_in_chunk(n, j, o.DT, o.window, o.KT);
-    for (int r = 0; r < nt; ++r) ++cnt[tgt_block_halves(cq0, cq1, r * o.KT + o.window)][tid];
+    // a tile is full (its block starts at the chunk's first row) when its
+    // first future row t0 + w is at most cq0 + 31: the first nfull tiles, all
+    // of one size; the others (at most DT/KT + 1) each have a size of their own
+    const int lim = cq0 + 31 - o.window;
+    nfull = lim < 0 ? 0 : min(nt, lim / o.KT + 1);
+    cf = tgt_block_halves(cq0, cq1, cq0);
+    cnt[cf][tid] = (unsigned short)nfull;
+    for (int r = nfull; r < nt; ++r) ++cnt[tgt_block_halves(cq0, cq1, r * o.KT + o.window)][tid];
   }
   __syncthreads();
-  if (tid < nc) {
-    int a = 0;
-    for (int g = 0; g < ng; ++g) {
-      const int v = cnt[tid][g];
-      cnt[tid][g] = (unsigned short)a;
-      a += v;
+  // exclusive prefix over the groups, one class per wave at a time
+  for (int c = wave; c < nc; c += 4) {
+    int carry = 0;
+    for (int g0 = 0; g0 < ng; g0 += 64) {
+      const int g = g0 + lane;
+      const int v = g < ng ? cnt[c][g] : 0;
+      const int inc = wave_incl_scan(v);
+      if (g < ng) cnt[c][g] = (unsigned short)(carry + inc - v);
+      carry += __shfl(inc, 63);
     }
-    tot[tid] = a;
+    if (lane == 0) tot[c] = carry;
   }
   __syncthreads();
-  if (tid == 0) {
-    long long a = 0;
-    for (int c = nc - 1; c >= 0; --c) {
-      base[c] = a;
-      a += (long long)o.sx * tot[c];
+  // class bases, largest class first: a suffix sum over the classes
+  if (wave == 0) {
+    const int c = nc - 1 - lane;  // lane 0: the largest class
+    const long long v = c >= 0 ? (long long)o.sx * tot[c] : 0;
+    long long inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long u = __shfl_up(inc, d);
+      if (lane >= d) inc += u;
     }
+    if (c >= 0) base[c] = inc - v;
   }
   __syncthreads();
-  if (tid < ng && nt > 0) {
-    const unsigned long long gbits = ((unsigned long long)j << 16) | ((unsigned long long)gm[tid] << 48);
-    int prev = -1, run0 = 0;
-    for (int r = 0; r < nt; ++r) {
-      const int c = tgt_block_halves(cq0, cq1, r * o.KT + o.window);
-      if (c != prev) {
-        prev = c;
-        run0 = r;
+  if (m >= 0) {
+    const unsigned long long gbits = ((unsigned long long)j << 16) | ((unsigned long long)m << 48);
+    const long long atf = base[cf] + cnt[cf][tid];
+    // (positions past cap arise only when the device offsets describe more
+    // blocks than the host's copy; those entries are dropped)
+    for (int sq = 0; sq < o.sx; ++sq)
+      for (int r = 0; r < nfull; ++r) {
+        const long long at = atf + (long long)sq * tot[cf] + r;
+        if (at < o.cap) o.order[at] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
       }
-      const long long at = base[c] + cnt[c][tid] + (r - run0);
-      for (int sq = 0; sq < o.sx; ++sq)
-        o.order[at + (long long)sq * tot[c]] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
+    for (int r = nfull; r < nt; ++r) {
+      const int c = tgt_block_halves(cq0, cq1, r * o.KT + o.window);
+      for (int sq = 0; sq < o.sx; ++sq) {
+        const long long at = base[c] + cnt[c][tid] + (long long)sq * tot[c];
+        if (at < o.cap) o.order[at] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
+      }
     }
   }
 }
@@ -565,7 +611,7 @@ static long long tgt_blocks_bound(const ShapeInfo &s) {
 static bool tgt_ordered(const ShapeInfo &s) {
   const int DT = tgt_chunk(s.max_doc);
   const long long nseq = (long long)s.B * s.Hkv;
-  return nseq % 8 == 0 && nseq / 8 < 65536 && s.n_docs < 65536 && (s.cu == nullptr) == (s.cu_host == nullptr) &&
+  return nseq % 8 == 0 && nseq / 8 < 65536 && s.n_docs <= TGT_ORDER_MAX_GROUPS && (s.cu == nullptr) == (s.cu_host == nullptr) &&
          DT / 32 + 1 <= TGT_ORDER_CLASSES && tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536;
 }
 // Bytes of the table for any window and key tile, plus the alignment.
@@ -683,6 +729,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
     ord.KT = tp.kt;
     ord.sx = s.B * s.Hkv / 8;
     ord.n_groups = (int)tgt_groups(s, tp.DT);
+    ord.cap = (long long)ord.sx * tp.blocks_per_seq;
     tp.order = ord.order;
     tp.sx = ord.sx;
   }
