@@ -102,11 +102,10 @@ __host__ __device__ __forceinline__ int tgt_block_halves(int cq0, int cq1, int f
 // Entry = tile | chunk << 16 | sequence << 32 | document << 48.  The table is
 // the same for every XCD and is written by the first workgroup of
 // future_target_neg_lse, which runs before the target kernel on the stream.
-constexpr int TGT_ORDER_MAX_GROUPS = 256;          // (document, chunk) groups per sequence
-constexpr int TGT_ORDER_CLASSES = 1024 / 32 + 1;   // sizes 1 .. DT/32 halves, DT <= 1024
+constexpr int TGT_ORDER_MAX_GROUPS = 64;           // (document, chunk) groups per sequence: one per lane
 struct TgtOrder {
   unsigned long long *order;  // [cap = sx * blocks_per_seq], or nullptr: no table
-  long long cap;              // entries; the builder writes none past it
+  int cap;                    // entries; the builder writes none past it
   const int *cu;
   int n_docs, S, DT, window, KT, sx, n_groups;
 };
@@ -122,103 +121,91 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// One workgroup of 256 threads; every phase is parallel (threads over
-// groups, waves over classes), so the table is ready in a few microseconds.
+// Written by the four waves of one workgroup without LDS (which the host
+// kernel's other workgroups would then reserve too): lane g of every wave
+// owns group g (at most 64 groups, checked on the host); per-class prefixes
+// over the groups and the class bases are wave scans.  Each wave computes
+// the same positions and writes a quarter of the entries.
+constexpr int TGT_ORDER_MAX_DIAG = 1024 / 128 + 1;  // tiles past the full ones in a group: <= DT/KT + 1
 __device__ void tgt_build_order(const TgtOrder &o) {
-  __shared__ int dlen[TGT_ORDER_MAX_GROUPS], dgrp[TGT_ORDER_MAX_GROUPS];
-  // per size class and group: tiles of that size, then their exclusive
-  // prefix over the groups (each < 65536: the host bounds a sequence's blocks)
-  __shared__ unsigned short cnt[TGT_ORDER_CLASSES][TGT_ORDER_MAX_GROUPS];
-  __shared__ int tot[TGT_ORDER_CLASSES];
-  __shared__ long long base[TGT_ORDER_CLASSES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ng = o.n_groups, nc = o.DT / 32 + 1;
-  // documents: lengths and their first group (groups run document by
-  // document, chunks descending)
-  if (tid < o.n_docs) dlen[tid] = o.cu != nullptr ? o.cu[tid + 1] - o.cu[tid] : o.S;
-  for (int i = tid; i < TGT_ORDER_CLASSES * TGT_ORDER_MAX_GROUPS; i += 256) (&cnt[0][0])[i] = 0;
-  if (wave == 0) {
-    // group offsets of documents 0..255, 64 at a time
-    int carry = 0;
-    for (int d0 = 0; d0 < o.n_docs; d0 += 64) {
-      const int d = d0 + lane;
-      const int v = d < o.n_docs ? (o.cu != nullptr ? o.cu[d + 1] - o.cu[d] : o.S) : 0;
-      const int c = v > 0 ? (v + o.DT - 1) / o.DT : 0;
-      const int inc = wave_incl_scan(c);
-      if (d < o.n_docs) dgrp[d] = carry + inc - c;
-      carry += __shfl(inc, 63);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // documents (lane d): length and first group; groups run document by
+  // document, chunks descending
+  int dl = 0, dc = 0;
+  if (lane < o.n_docs) {
+    dl = o.cu != nullptr ? o.cu[lane + 1] - o.cu[lane] : o.S;
+    dc = dl > 0 ? (dl + o.DT - 1) / o.DT : 0;
+  }
+  const int dg = wave_incl_scan(dc) - dc;
+  // this lane's group: the last non-empty document whose first group is <= lane
+  int m = -1, mlen = 0, mdg = 0;
+  for (int d = 0; d < o.n_docs; ++d) {
+    const int gd = __shfl(dg, d), ld = __shfl(dl, d);
+    if (gd <= lane && ld > 0) {
+      m = d;
+      mlen = ld;
+      mdg = gd;
     }
   }
-  __syncthreads();
-  // this thread's group: document m (the last whose first group is <= tid)
-  // and chunk j, counting chunks down from the document's last
-  int m = -1, j = 0, cq0 = 0, cq1 = 0, nt = 0, nfull = 0, cf = 0;
-  if (tid < ng) {
-    for (int d = 0; d < o.n_docs; ++d)
-      if (dgrp[d] <= tid && dlen[d] > 0) m = d;
-  }
-  if (m >= 0) {
-    const int n = dlen[m];
-    j = (n + o.DT - 1) / o.DT - 1 - (tid - dgrp[m]);
-    if (j < 0) m = -1;  // device offsets disagree with the host's: no tiles
-  }
-  if (m >= 0) {
-    const int n = dlen[m];
+  int j = m >= 0 ? (mlen + o.DT - 1) / o.DT - 1 - (lane - mdg) : -1;
+  const bool valid = lane < o.n_groups && m >= 0 && j >= 0;  // else: offsets disagree with the host's
+  int cq0 = 0, cq1 = 0, nt = 0, nfull = 0, cf = -1;
+  if (valid) {
     cq0 = j * o.DT;
-    cq1 = min(n, cq0 + o.DT);
-    nt = tgt_tiles_in_chunk(n, j, o.DT, o.window, o.KT);
+    cq1 = min(mlen, cq0 + o.DT);
+    nt = tgt_tiles_in_chunk(mlen, j, o.DT, o.window, o.KT);
     // a tile is full (its block starts at the chunk's first row) when its
     // first future row t0 + w is at most cq0 + 31: the first nfull tiles, all
-    // of one size; the others (at most DT/KT + 1) each have a size of their own
+    // of one size; the others each have a size of their own
     const int lim = cq0 + 31 - o.window;
     nfull = lim < 0 ? 0 : min(nt, lim / o.KT + 1);
-    cf = tgt_block_halves(cq0, cq1, cq0);
-    cnt[cf][tid] = (unsigned short)nfull;
-    for (int r = nfull; r < nt; ++r) ++cnt[tgt_block_halves(cq0, cq1, r * o.KT + o.window)][tid];
+    cf = nfull > 0 ? tgt_block_halves(cq0, cq1, cq0) : -1;
   }
-  __syncthreads();
-  // exclusive prefix over the groups, one class per wave at a time
-  for (int c = wave; c < nc; c += 4) {
-    int carry = 0;
-    for (int g0 = 0; g0 < ng; g0 += 64) {
-      const int g = g0 + lane;
-      const int v = g < ng ? cnt[c][g] : 0;
-      const int inc = wave_incl_scan(v);
-      if (g < ng) cnt[c][g] = (unsigned short)(carry + inc - v);
-      carry += __shfl(inc, 63);
-    }
-    if (lane == 0) tot[c] = carry;
-  }
-  __syncthreads();
-  // class bases, largest class first: a suffix sum over the classes
-  if (wave == 0) {
-    const int c = nc - 1 - lane;  // lane 0: the largest class
-    const long long v = c >= 0 ? (long long)o.sx * tot[c] : 0;
-    long long inc = v;
+  const int nd = min(nt - nfull, TGT_ORDER_MAX_DIAG);
+  int dcls[TGT_ORDER_MAX_DIAG];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const long long u = __shfl_up(inc, d);
-      if (lane >= d) inc += u;
+  for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k)
+    dcls[k] = k < nd ? tgt_block_halves(cq0, cq1, (nfull + k) * o.KT + o.window) : -1;
+  // classes from the largest down: the running base is the number of
+  // entries of all larger classes
+  int basec = 0, pos_f = 0, tot_f = 0;  // the host keeps the table below 2^31 entries
+  int pos_d[TGT_ORDER_MAX_DIAG], tot_d[TGT_ORDER_MAX_DIAG];
+#pragma unroll
+  for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k) pos_d[k] = tot_d[k] = 0;
+  for (int c = o.DT / 32; c >= 1; --c) {
+    int v = c == cf ? nfull : 0;
+#pragma unroll
+    for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k) v += dcls[k] == c ? 1 : 0;
+    const int incl = wave_incl_scan(v);
+    const int tot = __shfl(incl, 63);
+    const int at = basec + (incl - v);
+    if (c == cf) {
+      pos_f = at;
+      tot_f = tot;
     }
-    if (c >= 0) base[c] = inc - v;
+#pragma unroll
+    for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k)
+      if (dcls[k] == c) {
+        pos_d[k] = at;
+        tot_d[k] = tot;
+      }
+    basec += o.sx * tot;
   }
-  __syncthreads();
-  if (m >= 0) {
-    const unsigned long long gbits = ((unsigned long long)j << 16) | ((unsigned long long)m << 48);
-    const long long atf = base[cf] + cnt[cf][tid];
-    // (positions past cap arise only when the device offsets describe more
-    // blocks than the host's copy; those entries are dropped)
-    for (int sq = 0; sq < o.sx; ++sq)
-      for (int r = 0; r < nfull; ++r) {
-        const long long at = atf + (long long)sq * tot[cf] + r;
-        if (at < o.cap) o.order[at] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
-      }
-    for (int r = nfull; r < nt; ++r) {
-      const int c = tgt_block_halves(cq0, cq1, r * o.KT + o.window);
-      for (int sq = 0; sq < o.sx; ++sq) {
-        const long long at = base[c] + cnt[c][tid] + (long long)sq * tot[c];
-        if (at < o.cap) o.order[at] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
-      }
+  if (!valid) return;
+  // (positions past cap arise only when the device offsets describe more
+  // blocks than the host's copy; those entries are dropped)
+  const unsigned long long gbits = ((unsigned long long)j << 16) | ((unsigned long long)m << 48);
+  for (int sq = 0; sq < o.sx; ++sq) {
+    for (int r = wave; r < nfull; r += 4) {
+      const int at = pos_f + sq * tot_f + r;
+      if (at < o.cap) o.order[at] = gbits | (unsigned)r | ((unsigned long long)sq << 32);
     }
+#pragma unroll
+    for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k)
+      if (k < nd && (k & 3) == wave) {
+        const int at = pos_d[k] + sq * tot_d[k];
+        if (at < o.cap) o.order[at] = gbits | (unsigned)(nfull + k) | ((unsigned long long)sq << 32);
+      }
   }
 }
 
@@ -612,7 +599,8 @@ static bool tgt_ordered(const ShapeInfo &s) {
   const int DT = tgt_chunk(s.max_doc);
   const long long nseq = (long long)s.B * s.Hkv;
   return nseq % 8 == 0 && nseq / 8 < 65536 && s.n_docs <= TGT_ORDER_MAX_GROUPS && (s.cu == nullptr) == (s.cu_host == nullptr) &&
-         DT / 32 + 1 <= TGT_ORDER_CLASSES && tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536;
+         DT <= 1024 && tgt_groups(s, DT) <= TGT_ORDER_MAX_GROUPS && tgt_blocks_bound(s) < 65536 &&
+         nseq / 8 * tgt_blocks_bound(s) < 2147483647ll;
 }
 // Bytes of the table for any window and key tile, plus the alignment.
 static size_t tgt_order_bytes(const ShapeInfo &s) {
@@ -729,7 +717,7 @@ hipError_t launch_future_target(const ShapeInfo &s, const void *q, const void *k
     ord.KT = tp.kt;
     ord.sx = s.B * s.Hkv / 8;
     ord.n_groups = (int)tgt_groups(s, tp.DT);
-    ord.cap = (long long)ord.sx * tp.blocks_per_seq;
+    ord.cap = ord.sx * tp.blocks_per_seq;
     tp.order = ord.order;
     tp.sx = ord.sx;
   }
