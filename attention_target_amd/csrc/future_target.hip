@@ -167,12 +167,23 @@ __device__ void tgt_build_order(const TgtOrder &o) {
   for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k)
     dcls[k] = k < nd ? tgt_block_halves(cq0, cq1, (nfull + k) * o.KT + o.window) : -1;
   // classes from the largest down: the running base is the number of
-  // entries of all larger classes
+  // entries of all larger classes.  Only the classes some group holds are
+  // scanned (a few of the DT/32 sizes): each scan is a chain of cross-lane
+  // steps.
   int basec = 0, pos_f = 0, tot_f = 0;  // the host keeps the table below 2^31 entries
   int pos_d[TGT_ORDER_MAX_DIAG], tot_d[TGT_ORDER_MAX_DIAG];
 #pragma unroll
   for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k) pos_d[k] = tot_d[k] = 0;
-  for (int c = o.DT / 32; c >= 1; --c) {
+  unsigned long long held = cf > 0 ? 1ull << cf : 0ull;  // classes are 1 .. DT/32 <= 32
+#pragma unroll
+  for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k) held |= dcls[k] > 0 ? 1ull << dcls[k] : 0ull;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) held |= __shfl_xor(held, d);
+  unsigned long long todo = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(held >> 32)) << 32) |
+                            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)held);
+  while (todo != 0ull) {
+    const int c = 63 - __builtin_clzll(todo);
+    todo &= ~(1ull << c);
     int v = c == cf ? nfull : 0;
 #pragma unroll
     for (int k = 0; k < TGT_ORDER_MAX_DIAG; ++k) v += dcls[k] == c ? 1 : 0;
