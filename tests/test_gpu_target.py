@@ -134,6 +134,28 @@ def test_target_block_order(kvpop_lib, B, S, Hq, Hkv, D, docs, w):
         say(f"  {agg} mean={mean}: target err {e:.2e}")
 
 
+@pytest.mark.parametrize("n_docs", [16, 17])
+def test_target_block_order_group_limit(kvpop_lib, n_docs):
+    """Packed documents of 768 tokens (four 192-query chunks each): 16 give
+    64 (document, chunk) groups, the most the block-order table takes; 17
+    give 68 and run in the enumeration order.  Both against the oracle, with
+    the workspace filled with all-ones bytes first."""
+    S, Hq, Hkv, D, w = 768 * n_docs, 8, 8, 64, 50
+    say(f"block order at the group limit: {n_docs} documents of 768")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, "bf16", 70 + n_docs, device=DEV, heavy_hitters=True)
+    cu = synth.cu_seqlens_from_lengths([768] * n_docs)
+    cl = cu.tolist()
+    q, k = t["q"], t["k"]
+    r = oracle_ref(q, k, None, cl, w, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    need = kvpop_lib.workspace_size(kvpop_lib.CALL_FUTURE_TARGET, q, k, cu_seqlens=cu, window=w)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    tg = kvpop_lib.future_target(q, k, lse, w, cu_seqlens=cu, workspace=ws)
+    torch.cuda.synchronize()
+    e = assert_target_close(tg, dense.target_from_colmass(r["colmass"], Hkv, cl, w, dense.AGG_SUM))
+    say(f"  target err {e:.2e}")
+
+
 @pytest.mark.parametrize("kind,docs", [("rising", 1), ("jumps", 1), ("jumps", 3), ("falling", 1),
                                        ("negative", 1), ("negative", 4)])
 def test_forward_running_maximum(kvpop_lib, kind, docs):
