@@ -156,6 +156,30 @@ def test_target_block_order_group_limit(kvpop_lib, n_docs):
     say(f"  target err {e:.2e}")
 
 
+def test_target_block_order_short_documents(kvpop_lib):
+    """Packed documents shorter than the window (50, 30 and 64 tokens with
+    w = 100: their groups hold no blocks) between longer ones, in the
+    block-order table's layout (8 KV heads, batch 1); every aggregation
+    against the oracle, workspace filled with all-ones bytes first."""
+    lens = [50, 700, 30, 1200, 64, 333]
+    S, Hq, Hkv, D, w = sum(lens), 16, 8, 64, 100
+    say(f"block order with short documents {lens}")
+    t = synth.make_qkv(1, S, Hq, Hkv, D, "bf16", 404, device=DEV, heavy_hitters=True)
+    cu = synth.cu_seqlens_from_lengths(lens)
+    cl = cu.tolist()
+    q, k = t["q"], t["k"]
+    r = oracle_ref(q, k, None, cl, w, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    need = kvpop_lib.workspace_size(kvpop_lib.CALL_FUTURE_TARGET, q, k, cu_seqlens=cu, window=w)
+    for agg, mean in [("sum", False), ("none", True)]:
+        ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+        tg = kvpop_lib.future_target(q, k, lse, w, agg=agg, mean_over_queries=mean, cu_seqlens=cu, workspace=ws)
+        torch.cuda.synchronize()
+        ref = dense.target_from_colmass(r["colmass"], Hkv, cl, w, AGG[agg], mean, 0.0)
+        e = assert_target_close(tg, ref, what=f"target[{agg}]")
+        say(f"  {agg} mean={mean}: target err {e:.2e}")
+
+
 @pytest.mark.parametrize("kind,docs", [("rising", 1), ("jumps", 1), ("jumps", 3), ("falling", 1),
                                        ("negative", 1), ("negative", 4)])
 def test_forward_running_maximum(kvpop_lib, kind, docs):
