@@ -158,6 +158,28 @@ def attention_pass(q, k, v=None, cu=None, scale=None, window: Optional[int] = No
     return {"lse": lse, "out": out, "colmass": colmass, "abs_out": abs_out}
 
 
+def row_lse(q, k, rows, cu=None, scale=None, heads: Optional[list] = None) -> np.ndarray:
+    """The causal log-normaliser L^g_d of attention_pass for the listed query
+    positions only, one row at a time (for long sequences, where the whole
+    matrix is too large to build).  Returns [B, Hq, S] with NaN outside the
+    listed rows and heads."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    sc = default_scale(D, scale)
+    start, _ = doc_bounds(S, cu)
+    lse = np.full((B, Hq, S), np.nan)
+    if heads is None:
+        heads = [(b, g) for b in range(B) for g in range(Hq)]
+    for (b, g) in heads:
+        for d in sorted(set(int(x) for x in rows)):
+            r = np.array([d])
+            logits, allowed, _ = _causal_logits(q[b, g, r], k[b, g // G], r, start, sc)
+            lse[b, g, d] = _row_lse(logits, allowed)[0]
+    return lse
+
+
 def future_count(S: int, cu, window: int) -> np.ndarray:
     """N_t = number of queries d in t's document with d >= t + w."""
     _, end = doc_bounds(S, cu)
@@ -198,7 +220,7 @@ def target_from_colmass(colmass: np.ndarray, n_kv_heads: int, cu, window: int,
 
 
 def transposed_lse(q, k, lse: np.ndarray, cu=None, scale=None, window: int = 0,
-                   heads: Optional[list] = None, key_block: int = 256) -> np.ndarray:
+                   heads: Optional[list] = None, key_block: int = 256, keys=None) -> np.ndarray:
     """The pages' transposed-attention formulation of the first term of Eq. 8.
 
     [P] Section 3.2: original key positions become queries and original query
@@ -207,7 +229,8 @@ def transposed_lse(q, k, lse: np.ndarray, cu=None, scale=None, window: int = 0,
     and a block mask keeps d >= t + w; the LSE of that attention call, for
     key t, is ln sum_{d >= t+w} exp(s_{d,t} - L_d).  Returns that LSE,
     [B, Hq, S], natural log, -inf where no query qualifies.  Subtracting
-    ln N_t gives ln m^g(t) of Eq. 2.
+    ln N_t gives ln m^g(t) of Eq. 2.  `keys` restricts it to a list of key
+    positions (the others stay NaN).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -222,17 +245,18 @@ def transposed_lse(q, k, lse: np.ndarray, cu=None, scale=None, window: int = 0,
         h = g // G
         qs = q[b, g]                      # original queries act as keys here
         Lrow = np.asarray(lse[b, g], dtype=np.float64)
-        for t0 in range(0, S, key_block):
-            keys = np.arange(t0, min(S, t0 + key_block))
-            scores = sc * (k[b, h, keys] @ qs.T) - Lrow[None, :]   # score modifier -L_d
+        key_list = np.arange(S) if keys is None else np.array(sorted(set(int(x) for x in keys)), dtype=np.int64)
+        for t0 in range(0, key_list.size, key_block):
+            keys_b = key_list[t0:t0 + key_block]
+            scores = sc * (k[b, h, keys_b] @ qs.T) - Lrow[None, :]   # score modifier -L_d
             dcol = np.arange(S)
-            block_mask = (dcol[None, :] >= keys[:, None] + window) & (dcol[None, :] < end[keys][:, None]) \
-                & (dcol[None, :] >= start[keys][:, None])
+            block_mask = (dcol[None, :] >= keys_b[:, None] + window) & (dcol[None, :] < end[keys_b][:, None]) \
+                & (dcol[None, :] >= start[keys_b][:, None])
             masked = np.where(block_mask, scores, -np.inf)
             mx = masked.max(axis=1)
             mx_safe = np.where(np.isfinite(mx), mx, 0.0)
             with np.errstate(under="ignore", divide="ignore"):
-                res[b, g, keys] = mx_safe + np.log(np.exp(masked - mx_safe[:, None]).sum(axis=1))
+                res[b, g, keys_b] = mx_safe + np.log(np.exp(masked - mx_safe[:, None]).sum(axis=1))
     return res
 
 

@@ -3,6 +3,7 @@ against the fp64 CPU oracle, on seeded synthetic inputs.  Runs on an MI355X."""
 import math
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -178,6 +179,36 @@ def test_target_block_order_short_documents(kvpop_lib):
         ref = dense.target_from_colmass(r["colmass"], Hkv, cl, w, AGG[agg], mean, 0.0)
         e = assert_target_close(tg, ref, what=f"target[{agg}]")
         say(f"  {agg} mean={mean}: target err {e:.2e}")
+
+
+@pytest.mark.parametrize("S", [65536, 66000])
+def test_long_sequence_sampled(kvpop_lib, S):
+    """Long single sequences, checked on samples (the whole matrix is too
+    large for the oracle): 64 query rows per head against the oracle's row
+    LSE, and the per-head target on 64 keys per head against the oracle's
+    transposed LSE fed with the kernel's LSE (which the first check bounds).
+    S=65536 in 1024-query chunks is 64 (document, chunk) groups, the most the
+    block-order table takes; S=66000 is 65 and runs in the enumeration order.
+    The workspace starts as all-ones bytes."""
+    B, H, D, w = 1, 8, 64, 128
+    say(f"long sequence S={S}")
+    t = synth.make_qkv(B, S, H, H, D, "bf16", 31 + S, device=DEV, heavy_hitters=True)
+    q, k, v = t["q"], t["k"], t["v"]
+    _, lse = kvpop_lib.attn_fwd_lse(q, k, v, need_output=False)
+    need = kvpop_lib.workspace_size(kvpop_lib.CALL_FUTURE_TARGET, q, k, window=w)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    tg = kvpop_lib.future_target(q, k, lse, w, agg="none", workspace=ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(tg).any(), "a block left its partial unwritten"
+    r = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([r.integers(0, S, 60), [0, 1, S - 2, S - 1]]))
+    keys = np.unique(np.concatenate([r.integers(0, S - w, 60), [0, S - w - 1, S - w, S - 1]]))
+    q64, k64 = dense.to_f64(q), dense.to_f64(k)
+    ref_l = dense.row_lse(q64, k64, rows)
+    ref_t = dense.transposed_lse(q64, k64, lse.cpu().numpy(), window=w, keys=keys)
+    e1 = assert_lse_close(lse[:, :, rows], ref_l[:, :, rows], what="sampled lse")
+    e2 = assert_target_close(tg[:, :, keys], ref_t[:, :, keys], what="sampled target")
+    say(f"  lse err {e1:.2e}, target err {e2:.2e}")
 
 
 @pytest.mark.parametrize("kind,docs", [("rising", 1), ("jumps", 1), ("jumps", 3), ("falling", 1),

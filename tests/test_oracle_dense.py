@@ -84,6 +84,30 @@ def test_against_brute_force(S, D, G, docs, w, seed):
     assert np.allclose(r["colmass"], np.array(bc), rtol=1e-11, atol=1e-14)
 
 
+@settings(max_examples=20, deadline=None)
+@given(S=st.integers(1, 24), D=st.sampled_from([2, 4]), G=st.sampled_from([1, 2]),
+       docs=st.integers(1, 3), w=st.integers(0, 26), seed=st.integers(0, 10_000))
+def test_row_and_key_subsets_against_brute_force(S, D, G, docs, w, seed):
+    """The subset forms used for long sequences: row_lse on a few query rows,
+    and transposed_lse on a few keys fed with the dense L (ln of the column
+    mass by Eq. 8), against the pure-Python double sums; other entries NaN."""
+    q, k, v = rand_problem(1, G, 1, S, D, seed, scale_k=1.5)
+    cu = rand_cu(S, min(docs, S), seed + 1)
+    bl, _, bc = brute.brute_attention(q.tolist(), k.tolist(), v.tolist(), cu=cu, window=w)
+    bl = np.array(bl)
+    r = np.random.default_rng(seed)
+    rows = r.choice(S, size=min(S, 5), replace=False)
+    got = dense.row_lse(q, k, rows, cu=cu)
+    assert np.allclose(got[:, :, rows], bl[:, :, rows], rtol=1e-12, atol=1e-12)
+    assert np.all(np.isnan(np.delete(got, rows, axis=2)))
+    keys = r.choice(S, size=min(S, 5), replace=False)
+    tl = dense.transposed_lse(q, k, bl, cu=cu, window=w, keys=keys)
+    with np.errstate(divide="ignore"):
+        want = np.log(np.array(bc))
+    assert np.allclose(tl[:, :, keys], want[:, :, keys], rtol=1e-11, atol=1e-12)
+    assert np.all(np.isnan(np.delete(tl, keys, axis=2)))
+
+
 # ---------------------------------------------------------------- library routine
 @pytest.mark.parametrize("docs", [1, 3])
 def test_against_torch_sdpa(docs):
