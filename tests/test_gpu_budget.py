@@ -270,6 +270,25 @@ def test_budget32k(kvpop_lib):
                  heads=[(0, g) for g in range(32)], rows=rows)
 
 
+@pytest.mark.parametrize("S,packed", [(40000, False), (36000, True)])
+def test_budget_long_sequence(kvpop_lib, S, packed):
+    """Past 32768 eligible tokens (S=40000 minus 4 sinks; or packed, where the
+    wavelet matrix spans the whole sequence) the wavelet matrix is built by
+    the sequential global-memory kernel instead of in LDS.  Ranks, cutoffs
+    and the key lists of every block exactly; output and LSE of every query
+    head on sampled rows."""
+    Hq, Hkv = 4, 1
+    cu = [0, 9000, 9100, 30000, S] if packed else None
+    say(f"budget long sequence S={S} packed={packed}")
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 40 + S, device=DEV, with_scores=True)
+    r = np.random.default_rng(S)
+    rows = np.concatenate([np.arange(32), np.arange(S - 32, S), r.integers(0, S, 192)])
+    if packed:
+        rows = np.concatenate([rows, [8999, 9000, 9099, 9100, 29999, 30000]])
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], t["scores"], 4, 128, 1916,
+                 heads=[(0, g) for g in range(Hq)], rows=rows, cu=cu)
+
+
 # Packed documents: each document keeps what it would keep alone (sinks and
 # window counted from its start).  Document lengths include ones shorter
 # than a query block (32 positions), than the sinks plus window, and one.
