@@ -118,6 +118,8 @@ SMALL = [
     (2500, 4, 1, 128, "bf16", 4, 128, 300, "increasing"),
     (640, 6, 2, 128, "bf16", 4, 32, 90, "normal"),     # G = 3: 128-query blocks, three per KV head
     (520, 12, 2, 64, "bf16", 2, 16, 60, "ties"),       # G = 6: 64-query blocks, three per KV head
+    (600, 16, 2, 128, "bf16", 4, 32, 90, "normal"),    # G = 8: 32-query blocks, two per KV head
+    (450, 5, 1, 64, "bf16", 2, 16, 40, "ties"),        # G = 5: 128-query blocks, five per KV head
 ]
 
 

@@ -39,6 +39,9 @@ CASES = [
     (300, 2, 1, 64, "bf16", 1, 8, 1),       # one top-k slot: an eviction leaves no other key
     (250, 4, 2, 128, "bf16", 0, 1, 5),      # one-token window: a ring of two slots
     (600, 8, 2, 128, "f32", 4, 32, 150),    # fp32 at head_dim 128, several chunks
+    (230, 5, 1, 64, "bf16", 2, 16, 30),     # 5 query heads per KV head
+    (260, 12, 2, 128, "bf16", 3, 8, 40),    # 6 query heads per KV head
+    (210, 7, 1, 64, "bf16", 1, 4, 90),      # 7 query heads per KV head
 ]
 
 

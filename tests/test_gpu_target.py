@@ -75,6 +75,9 @@ CASES = [
     (1100, 4, 1, 128, "bf16", 2, 128),
     (450, 6, 2, 128, "bf16", 2, 32),    # G = 3: one head per block, three blocks per KV head
     (390, 12, 2, 64, "bf16", 1, 7),     # G = 6: two heads per block, three blocks per KV head
+    (300, 16, 2, 64, "bf16", 1, 8),     # G = 8: four heads per block, two blocks per KV head
+    (257, 16, 1, 128, "bf16", 2, 5),    # G = 16: four blocks per KV head, two documents
+    (400, 5, 1, 64, "bf16", 1, 3),      # G = 5: one head per block, five blocks per KV head
 ]
 
 
