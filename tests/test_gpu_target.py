@@ -265,6 +265,25 @@ def test_target_fp32_head_dim_128(kvpop_lib):
         assert_target_close(tg, ref, what=f"target fp32 D=128 {agg}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_target_fp32_large_grid(kvpop_lib, D):
+    """fp32 Q and K on a grid of more than 2048 blocks (B=2, 4 KV heads,
+    S=8192: 256-key blocks, 512-query chunks, and the block-order table),
+    fed with the oracle's LSE: SUM and per-head targets on every key."""
+    B, Hq, Hkv, S, w = 2, 4, 4, 8192, 64
+    say(f"fp32 target, large grid, D={D}")
+    t = synth.make_qkv(B, S, Hq, Hkv, D, "f32", 90 + D, device=DEV)
+    q, k = t["q"], t["k"]
+    r = oracle_ref(q, k, None, None, w, need_output=False)
+    lse = torch.from_numpy(r["lse"]).to(torch.float32).to(DEV)
+    for agg, code in (("sum", dense.AGG_SUM), ("none", dense.AGG_NONE)):
+        tg = kvpop_lib.future_target(q, k, lse, w, agg=agg)
+        torch.cuda.synchronize()
+        ref = dense.target_from_colmass(r["colmass"], Hkv, None, w, code)
+        e = assert_target_close(tg, ref, what=f"target fp32 D={D} {agg}")
+        say(f"  {agg}: target err {e:.2e}")
+
+
 def test_qwen4k_full(kvpop_lib):
     """S=4096, 32q/8kv, D=128, bf16, 1% heavy hitters, w=64: every head."""
     t = to_dev(synth.make_workload("qwen4k", device=DEV))
