@@ -40,6 +40,7 @@ struct FwdParams {
   const int *list_len;       // [B*Hkv][nqb]
   const int *list_len_full;  // [B*Hkv][nqb]: leading entries kept by every query of the block
   int list_cap;
+  const int *qorder;  // [B*Hkv][nqb]: the order in which query blocks run (packed documents), or nullptr
 };
 
 #ifndef KVPOP_FWD_KT
@@ -161,11 +162,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVPOP_
   const int HG = p.HG, QB = 32 * (4 / HG), NG = p.G / HG;
   const int nqb = (p.S + QB - 1) / QB;
   const int per_qb = p.B * p.Hkv * NG;
-  const int qb = nqb - 1 - (int)blockIdx.x / per_qb;  // latest (heaviest) query blocks first
+  int qb = nqb - 1 - (int)blockIdx.x / per_qb;  // latest (heaviest) query blocks first
   int rr = (int)blockIdx.x % per_qb;
   const int ng = rr % NG;
   rr /= NG;
   const int h = rr % p.Hkv, b = rr / p.Hkv;
+  // over packed documents a budget list's length follows the block's
+  // position in its document, so those blocks run in the order of a table
+  // sorted by list length
+  if constexpr (SPARSE) {
+    if (p.qorder != nullptr) qb = p.qorder[((size_t)b * p.Hkv + h) * nqb + (int)blockIdx.x / per_qb];
+  }
   const int g = h * p.G + ng * HG + wave % HG;
   const int q0 = qb * QB + 32 * (wave / HG);  // first query of this wave
   const int qpos = q0 + col;

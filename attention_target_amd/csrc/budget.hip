@@ -39,7 +39,7 @@ constexpr int CUT_NONE = -1;
 
 struct BudgetLayout {
   size_t sorted, rank, order, cutoff, arr0, arr1, bits, prefix, zeros, lists, spans, lens, lens_full, lstatus,
-      total;
+      qorder, total;
   int S_pad, nchunks, L, nw1, nqb, QB, cap;
 };
 
@@ -80,6 +80,7 @@ static BudgetLayout budget_layout(const ShapeInfo &s, int sinks, int window, int
   lo.lens = take(BH * lo.nqb * 4);
   lo.lens_full = take(BH * lo.nqb * 4);
   lo.lstatus = take(BH * lo.nqb * 4);
+  lo.qorder = take(BH * lo.nqb * 4);
   lo.total = off;
   return lo;
 }
@@ -742,6 +743,32 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
   }
 }
 
+// The order of the sparse forward's query blocks over packed documents.  A
+// block's work is its list, whose length follows the block's position inside
+// its document rather than in the sequence, so latest-first is no longer
+// largest-first: blocks are ranked by tile count (descending), later blocks
+// first among equals (the order without documents), and run in that order,
+// which puts the short lists of early and short documents in the last
+// round.  One workgroup per (batch row, KV head); each thread ranks its
+// blocks against all of the head's tile counts, held in LDS.
+constexpr int BLOCK_ORDER_MAX = 1024;  // query blocks per head the ranking takes
+__global__ void __launch_bounds__(256) budget_block_order(const int *lens, int *qorder, int nqb, int KT) {
+  __shared__ unsigned short tl[BLOCK_ORDER_MAX];
+  const size_t bh = blockIdx.x;
+  if (nqb > BLOCK_ORDER_MAX) return;  // the host launches this only when the head's blocks fit
+  for (int i = threadIdx.x; i < nqb; i += 256) tl[i] = (unsigned short)((lens[bh * nqb + i] + KT - 1) / KT);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nqb; i += 256) {
+    const int ti = tl[i];
+    int r = 0;
+    for (int j = 0; j < nqb; ++j) {
+      const int tj = tl[j];
+      r += (tj > ti || (tj == ti && j > i)) ? 1 : 0;
+    }
+    qorder[bh * nqb + r] = i;
+  }
+}
+
 template <typename T, int D>
 static hipError_t run_sparse(const FwdParams &fp, int grid, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, true>), dim3(grid), dim3(256), 0, st, fp);
@@ -824,6 +851,12 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   fp.list_len = lp.lens;
   fp.list_len_full = lp.lens_full;
   fp.list_cap = lo.cap;
+  if (s.cu != nullptr && lo.nqb <= BLOCK_ORDER_MAX) {
+    fp.qorder = reinterpret_cast<int *>(w + lo.qorder);
+    hipLaunchKernelGGL(budget_block_order, dim3(BH), dim3(256), 0, st, lp.lens, reinterpret_cast<int *>(w + lo.qorder),
+                       lo.nqb, KVPOP_FWD_KT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int grid = lo.nqb * s.B * s.Hkv * (fp.G / fp.HG);
   if (s.dtype == 0 && s.D == 128) return run_sparse<bf16, 128>(fp, grid, st);
   if (s.dtype == 0 && s.D == 64) return run_sparse<bf16, 64>(fp, grid, st);
