@@ -749,23 +749,51 @@ __global__ void __launch_bounds__(256) budget_lists(const ListParams p) {
 // largest-first: blocks are ranked by tile count (descending), later blocks
 // first among equals (the order without documents), and run in that order,
 // which puts the short lists of early and short documents in the last
-// round.  One workgroup per (batch row, KV head); each thread ranks its
-// blocks against all of the head's tile counts, held in LDS.
+// round.  A block's rank is the number of the head's blocks ahead of it.
+// Each workgroup ranks 64 of one head's blocks (one per lane); its four
+// waves each count the blocks ahead within a quarter of the head's tile
+// counts, held in LDS, and the quarters' counts are summed.
 constexpr int BLOCK_ORDER_MAX = 1024;  // query blocks per head the ranking takes
-__global__ void __launch_bounds__(256) budget_block_order(const int *lens, int *qorder, int nqb, int KT) {
-  __shared__ unsigned short tl[BLOCK_ORDER_MAX];
-  const size_t bh = blockIdx.x;
-  if (nqb > BLOCK_ORDER_MAX) return;  // the host launches this only when the head's blocks fit
-  for (int i = threadIdx.x; i < nqb; i += 256) tl[i] = (unsigned short)((lens[bh * nqb + i] + KT - 1) / KT);
+constexpr int ORDER_ROWS = 64;         // blocks ranked per workgroup
+constexpr int ORDER_SLICES = 4;        // waves per workgroup, one slice of the counts each
+__global__ void __launch_bounds__(ORDER_ROWS *ORDER_SLICES) budget_block_order(const int *lens, int *qorder, int nqb,
+                                                                               int KT) {
+  __shared__ __align__(16) unsigned short tl[BLOCK_ORDER_MAX];
+  __shared__ int part[ORDER_SLICES][ORDER_ROWS];
+  if (nqb <= 0 || nqb > BLOCK_ORDER_MAX) return;  // the host launches this only when the head's blocks fit
+  const int per_head = (nqb + ORDER_ROWS - 1) / ORDER_ROWS;
+  const size_t bh = blockIdx.x / per_head;
+  const int i0 = (int)(blockIdx.x % per_head) * ORDER_ROWS;
+  // the table is padded to whole 8-count reads in every slice; padding holds 0
+  // and a real block 1 + its tile count (saturated at 16 bits), so padding is
+  // never ahead of a block and the ranks stay a permutation
+  constexpr int STEP = 8 * ORDER_SLICES;
+  const int npad = (nqb + STEP - 1) / STEP * STEP;  // <= BLOCK_ORDER_MAX, a multiple of STEP
+  for (int j = threadIdx.x; j < npad; j += ORDER_ROWS * ORDER_SLICES)
+    tl[j] = j < nqb ? (unsigned short)min((lens[bh * nqb + j] + KT - 1) / KT + 1, 0xffff) : 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < nqb; i += 256) {
-    const int ti = tl[i];
-    int r = 0;
-    for (int j = 0; j < nqb; ++j) {
-      const int tj = tl[j];
-      r += (tj > ti || (tj == ti && j > i)) ? 1 : 0;
+  const int lane = threadIdx.x % ORDER_ROWS, slice = threadIdx.x / ORDER_ROWS;
+  const int i = i0 + lane;
+  const int ti = i < nqb ? (int)tl[i] : 0;
+  const int span = npad / ORDER_SLICES;
+  int r = 0;
+  // all lanes of a wave read the same eight counts at a time (a broadcast LDS read)
+  for (int j0 = slice * span; j0 < (slice + 1) * span; j0 += 8) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(&tl[j0]);
+    const unsigned wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tj = (int)((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      r += (int)(tj > ti) | ((int)(tj == ti) & (int)(j0 + e > i));
     }
-    qorder[bh * nqb + r] = i;
+  }
+  part[slice][lane] = r;
+  __syncthreads();
+  if (slice == 0 && i < nqb) {
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < ORDER_SLICES; ++q) rank += part[q][lane];
+    qorder[bh * nqb + rank] = i;
   }
 }
 
@@ -852,9 +880,11 @@ hipError_t launch_budget(const ShapeInfo &s, const void *q, const void *k, const
   fp.list_len_full = lp.lens_full;
   fp.list_cap = lo.cap;
   if (s.cu != nullptr && lo.nqb <= BLOCK_ORDER_MAX) {
-    fp.qorder = reinterpret_cast<int *>(w + lo.qorder);
-    hipLaunchKernelGGL(budget_block_order, dim3(BH), dim3(256), 0, st, lp.lens, reinterpret_cast<int *>(w + lo.qorder),
-                       lo.nqb, KVPOP_FWD_KT);
+    int *qorder = reinterpret_cast<int *>(w + lo.qorder);
+    fp.qorder = qorder;
+    const int per_head = (lo.nqb + ORDER_ROWS - 1) / ORDER_ROWS;
+    hipLaunchKernelGGL(budget_block_order, dim3(BH * per_head), dim3(ORDER_ROWS * ORDER_SLICES), 0, st, lp.lens,
+                       qorder, lo.nqb, KVPOP_FWD_KT);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int grid = lo.nqb * s.B * s.Hkv * (fp.G / fp.HG);
