@@ -291,6 +291,23 @@ def test_budget_long_sequence(kvpop_lib, S, packed):
                  heads=[(0, g) for g in range(Hq)], rows=rows, cu=cu)
 
 
+def test_budget_packed_block_order_limit(kvpop_lib):
+    """Packed S=32768 at 4 query heads per KV head: 1024 query blocks per
+    head, the most the budget forward still runs in list-length order (one
+    more block and it keeps the plain order, as at S=36000 above).  Ranks,
+    cutoffs and the key lists of every block exactly; output and LSE of
+    every query head on sampled rows."""
+    S, Hq, Hkv = 32768, 8, 2
+    cu = [0, 700, 13000, 13032, 20000, S]
+    say(f"budget packed S={S} docs={np.diff(cu).tolist()} Hq={Hq} Hkv={Hkv}")
+    t = synth.make_qkv(1, S, Hq, Hkv, 128, "bf16", 77, device=DEV, with_scores=True)
+    r = np.random.default_rng(S + 1)
+    rows = np.concatenate([np.arange(32), np.arange(S - 32, S), r.integers(0, S, 128),
+                           [699, 700, 12999, 13000, 13031, 13032, 19999, 20000]])
+    check_budget(kvpop_lib, t["q"], t["k"], t["v"], t["scores"], 4, 128, 1916,
+                 heads=[(0, g) for g in range(Hq)], rows=rows, cu=cu)
+
+
 # Packed documents: each document keeps what it would keep alone (sinks and
 # window counted from its start).  Document lengths include ones shorter
 # than a query block (32 positions), than the sinks plus window, and one.
