@@ -78,13 +78,33 @@ def blas_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
+_AHEAD = {}
+
+
+def queue_ahead(products: int = 8):
+    """Queue fp32 matrix products (about a millisecond each) on the current
+    stream, so that the host issues the work that follows while the GPU is
+    still busy: short calls then run back to back instead of waiting for
+    their launches."""
+    dev = torch.cuda.current_device()
+    if dev not in _AHEAD:
+        _AHEAD[dev] = torch.randn(4096, 4096, device=f"cuda:{dev}")
+        torch.mm(_AHEAD[dev], _AHEAD[dev])  # the first product loads the library's kernels
+        torch.cuda.synchronize()
+    a = _AHEAD[dev]
+    for _ in range(products):
+        torch.mm(a, a)
+
+
 def timed_calls(fns, reps: int, warm: int = 2):
     """Median milliseconds of each callable in `fns`, run in turn `warm` +
     `reps` times back to back on the current stream, HIP events between the
-    calls and one synchronisation at the end."""
+    calls and one synchronisation at the end.  The calls are issued behind
+    queued work, so each interval is the GPU's time for the call."""
     stream = torch.cuda.current_stream()
     n = len(fns)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(warm + reps)]
+    queue_ahead()
     for i in range(warm + reps):
         ev[i][0].record(stream)
         for j, f in enumerate(fns):
@@ -356,11 +376,8 @@ def decode_measurement(kv, dev, steps_fill: int = 2560, steps_timed: int = 200):
     us_host = e0.elapsed_time(e1) * 1e3 / steps_timed
     # GPU time: fp32 products queued ahead keep the GPU busy for milliseconds
     # while the host issues every timed step, which then run back to back
-    big = torch.randn(8192, 8192, device=dev)
-    torch.mm(big, big)  # the first product loads the library's kernels
     torch.cuda.synchronize()
-    for _ in range(4):
-        torch.mm(big, big)
+    queue_ahead(16)
     e0.record(stream)
     t0 = time.perf_counter()
     for i in range(steps_fill + steps_timed, n):
@@ -369,7 +386,6 @@ def decode_measurement(kv, dev, steps_fill: int = 2560, steps_timed: int = 200):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps_timed
-    del big
     return {"workload": f"one layer, batch {B_}, {Hq}q/{Hkv}kv, D={D}, bf16, budget {sinks}+{window}+{topk}=2048, "
                         f"steady state after {steps_fill} tokens",
             "us_per_step": round(us, 2), "us_per_step_host_paced": round(us_host, 2),
