@@ -335,91 +335,152 @@ __global__ void __launch_bounds__(1024) budget_wavelet_levels(const WaveletParam
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_e = p.S - p.base;
   if (n_e <= 0 || n_e > N_MAX || p.nw1 > WV_LDS_WORDS) return;  // host picks this kernel only when it fits
-  {
-    const int *src = p.rank + bh * p.S + p.base;
-    int r[WV_PER_THREAD];
-#pragma unroll
-    for (int j = 0; j < WV_PER_THREAD; ++j) r[j] = src[min(tid + 1024 * j, n_e - 1)];
-#pragma unroll
-    for (int j = 0; j < WV_PER_THREAD; ++j) arr[0][tid + 1024 * j] = (uint16_t)r[j];
-  }
-  for (int w = 32 * WV_PER_THREAD + tid; w < p.nw1; w += 1024) wl[w] = 0u;  // words past the ballots' reach
-  __syncthreads();
-  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
+  int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
   const int nb = p.L - 1 - lvl;  // key bits: bit L-1-kp of a rank is key bit kp
-  int cur = 0;
-  for (int pass = 0; 4 * pass < nb; ++pass) {
-    const uint16_t *a = arr[cur];
-    uint16_t *b = arr[cur ^ 1];
-    for (int e = tid; e < (NCNT + 8) / 2; e += 1024) reinterpret_cast<uint32_t *>(cnt)[e] = 0u;
+  if (lvl <= 1 && nb > 12 && (1 << p.L) <= N_MAX) {
+    // Levels 0 and 1 of a long range, which would take four radix passes.
+    // A key's bucket holds only the 2 or 4 rank values that differ in the
+    // bits at and below the level, so the level is built in one step: each
+    // rank value's position is tabulated, the buckets' counts are scanned in
+    // key order (the key being the bits above the level, reversed), and an
+    // element's slot is its key's first slot plus the members of its bucket
+    // that precede it in position.  Only the level's bit words are formed.
+    uint16_t *pos_of = arr[0];  // position of each rank value, 0xffff where absent
+    uint16_t *kbase = arr[1];   // first slot of each key
+    const int nv = 1 << p.L, nk = 1 << nb, bsz = 2 << lvl;
+    for (int x = tid; x < nv / 2; x += 1024) reinterpret_cast<uint32_t *>(pos_of)[x] = 0xffffffffu;
+    for (int w = tid; w < p.nw1; w += 1024) wl[w] = 0u;
     __syncthreads();
-    // per element: digit (4 bits) and rank among the group's equal digits
-    // (6 bits), two elements per register
-    uint32_t dr[WV_PER_THREAD / 2];
+    const int *src = p.rank + bh * p.S + p.base;
+    int v[WV_PER_THREAD];
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      // groups of eight reads: the compiler barrier keeps it from hoisting
-      // all of them (with the packed ranks they would exceed 128 registers)
-      if (j % 8 == 0) asm volatile("" ::: "memory");
-      const uint32_t v = a[tid + 1024 * j];
-      int d = 0;
+      const int i = tid + 1024 * j;
+      v[j] = i < n_e ? src[i] : 0;
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kp = 4 * pass + q;
-        if (kp < nb) d |= (int)((v >> (p.L - 1 - kp)) & 1u) << q;
-      }
-      d = (tid + 1024 * j < n_e) ? d : 15;
-      uint64_t m = ~0ull;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint64_t bq = __ballot((d >> q) & 1);
-        m &= ((d >> q) & 1) ? bq : ~bq;
-      }
-      const int rk = __popcll(m & below);
-      if (rk == 0) cnt[d * CS + 16 * j + wave] = (uint16_t)__popcll(m);  // the digit's lowest lane
-      const uint32_t e = (uint32_t)(d | (rk << 4));
-      dr[j / 2] = (j & 1) ? (dr[j / 2] | (e << 16)) : e;
+    for (int j = 0; j < WV_PER_THREAD; ++j) {
+      const int i = tid + 1024 * j;
+      if (i < n_e) pos_of[v[j]] = (uint16_t)i;  // ranks are distinct and below S <= nv
     }
     __syncthreads();
-    // exclusive scan of the counts, digit-major (a row's two pad entries are 0)
-    constexpr int PER = (NCNT + 1023) / 1024;
+    auto bucket_count = [&](int k) {
+      const int m = (int)(__brev((unsigned)k) >> (32 - nb));
+      int c = 0;
+      for (int u = 0; u < bsz; ++u) c += pos_of[m * bsz + u] != 0xffff ? 1 : 0;
+      return c;
+    };
+    const int kpt = (nk + 1023) / 1024;  // keys per thread, contiguous
     int local = 0;
-    for (int e = 0; e < PER; ++e) {
-      const int idx = tid * PER + e;
-      local += idx < NCNT ? cnt[idx] : 0;
+    for (int q = 0; q < kpt; ++q) {
+      const int k = tid * kpt + q;
+      if (k < nk) local += bucket_count(k);
     }
     int total;
     int run = block_excl_scan_1024(local, sh_waves, total);
-    for (int e = 0; e < PER; ++e) {  // each thread rewrites only its own entries
-      const int idx = tid * PER + e;
-      if (idx < NCNT) {
-        const int c = cnt[idx];
-        cnt[idx] = (uint16_t)run;
-        run += c;
+    for (int q = 0; q < kpt; ++q) {
+      const int k = tid * kpt + q;
+      if (k < nk) {
+        kbase[k] = (uint16_t)run;
+        run += bucket_count(k);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < WV_PER_THREAD; ++j) {
-      if (j % 8 == 0) asm volatile("" ::: "memory");
-      const uint32_t e = (dr[j / 2] >> (16 * (j & 1))) & 0xffffu;
-      const int d = (int)(e & 15u), rk = (int)(e >> 4);
-      const int pos = (int)cnt[d * CS + 16 * j + wave] + rk;
-      b[pos < N_MAX ? pos : N_MAX + lane] = a[tid + 1024 * j];
+      const int i = tid + 1024 * j;
+      if (i < n_e && ((v[j] >> lvl) & 1)) {
+        const int m = v[j] >> (lvl + 1);
+        int slot = kbase[__brev((unsigned)m) >> (32 - nb)];
+        for (int u = 0; u < bsz; ++u) slot += pos_of[m * bsz + u] < i ? 1 : 0;  // absent values read 0xffff
+        atomicOr(&wl[slot >> 5], 1u << (slot & 31));
+      }
     }
-    __syncthreads();
-    cur ^= 1;
-  }
-  // this level's bits of the arrangement, prefix counts and zero count
-  const uint16_t *a = arr[cur];
-  uint32_t *bl = p.bits + (bh * p.L + lvl) * p.nw1;
-  int *pl = p.prefix + (bh * p.L + lvl) * p.nw1;
+  } else {
+    {
+      const int *src = p.rank + bh * p.S + p.base;
+      int r[WV_PER_THREAD];
 #pragma unroll
-  for (int j = 0; j < WV_PER_THREAD; ++j) {
-    const int i = tid + 1024 * j;
-    const int bit = (i < n_e) ? (int)(a[i] >> lvl) & 1 : 0;
-    const uint64_t m = __ballot(bit);
-    wl[32 * j + 2 * wave + (lane & 1)] = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+      for (int j = 0; j < WV_PER_THREAD; ++j) r[j] = src[min(tid + 1024 * j, n_e - 1)];
+#pragma unroll
+      for (int j = 0; j < WV_PER_THREAD; ++j) arr[0][tid + 1024 * j] = (uint16_t)r[j];
+    }
+    for (int w = 32 * WV_PER_THREAD + tid; w < p.nw1; w += 1024) wl[w] = 0u;  // words past the ballots' reach
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    int cur = 0;
+    for (int pass = 0; 4 * pass < nb; ++pass) {
+      const uint16_t *a = arr[cur];
+      uint16_t *b = arr[cur ^ 1];
+      for (int e = tid; e < (NCNT + 8) / 2; e += 1024) reinterpret_cast<uint32_t *>(cnt)[e] = 0u;
+      __syncthreads();
+      // per element: digit (4 bits) and rank among the group's equal digits
+      // (6 bits), two elements per register
+      uint32_t dr[WV_PER_THREAD / 2];
+#pragma unroll
+      for (int j = 0; j < WV_PER_THREAD; ++j) {
+        // groups of eight reads: the compiler barrier keeps it from hoisting
+        // all of them (with the packed ranks they would exceed 128 registers)
+        if (j % 8 == 0) asm volatile("" ::: "memory");
+        const uint32_t v = a[tid + 1024 * j];
+        int d = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kp = 4 * pass + q;
+          if (kp < nb) d |= (int)((v >> (p.L - 1 - kp)) & 1u) << q;
+        }
+        d = (tid + 1024 * j < n_e) ? d : 15;
+        uint64_t m = ~0ull;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint64_t bq = __ballot((d >> q) & 1);
+          m &= ((d >> q) & 1) ? bq : ~bq;
+        }
+        const int rk = __popcll(m & below);
+        if (rk == 0) cnt[d * CS + 16 * j + wave] = (uint16_t)__popcll(m);  // the digit's lowest lane
+        const uint32_t e = (uint32_t)(d | (rk << 4));
+        dr[j / 2] = (j & 1) ? (dr[j / 2] | (e << 16)) : e;
+      }
+      __syncthreads();
+      // exclusive scan of the counts, digit-major (a row's two pad entries are 0)
+      constexpr int PER = (NCNT + 1023) / 1024;
+      int local = 0;
+      for (int e = 0; e < PER; ++e) {
+        const int idx = tid * PER + e;
+        local += idx < NCNT ? cnt[idx] : 0;
+      }
+      int total;
+      int run = block_excl_scan_1024(local, sh_waves, total);
+      for (int e = 0; e < PER; ++e) {  // each thread rewrites only its own entries
+        const int idx = tid * PER + e;
+        if (idx < NCNT) {
+          const int c = cnt[idx];
+          cnt[idx] = (uint16_t)run;
+          run += c;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < WV_PER_THREAD; ++j) {
+        if (j % 8 == 0) asm volatile("" ::: "memory");
+        const uint32_t e = (dr[j / 2] >> (16 * (j & 1))) & 0xffffu;
+        const int d = (int)(e & 15u), rk = (int)(e >> 4);
+        const int pos = (int)cnt[d * CS + 16 * j + wave] + rk;
+        b[pos < N_MAX ? pos : N_MAX + lane] = a[tid + 1024 * j];
+      }
+      __syncthreads();
+      cur ^= 1;
+    }
+    // this level's bits of the arrangement
+    const uint16_t *a = arr[cur];
+#pragma unroll
+    for (int j = 0; j < WV_PER_THREAD; ++j) {
+      const int i = tid + 1024 * j;
+      const int bit = (i < n_e) ? (int)(a[i] >> lvl) & 1 : 0;
+      const uint64_t m = __ballot(bit);
+      wl[32 * j + 2 * wave + (lane & 1)] = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+    }
   }
   __syncthreads();
   const int wpt = (p.nw1 + 1023) / 1024;  // words per thread in the scan
